@@ -1,0 +1,138 @@
+"""Linear cross-entropy (``inputs @ weight.T`` then cross-entropy), in fp64 on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Follows the greyhound functional API page, ``chunked_linear_loss`` and
+``chunked_linear_cross_entropy``:
+
+* the logits are ``inputs [BT, D] @ weight[V, D].T``;
+* the loss is the ``cross_entropy`` of those logits (``oracle.ce``), with
+  ``mean`` dividing by the number of valid tokens of the whole batch (the
+  plain reading: one global N, not a mean of per-chunk means);
+* ``grad_inputs = G @ weight`` and ``grad_weight = G.T @ inputs`` where ``G`` is
+  the logits gradient; chunking the rows changes neither in exact arithmetic,
+  so the fp32-accumulation mode is the exact product;
+* ``grad_weight_accum_dtype='weight'`` accumulates directly in the parameter
+  dtype and rounds between chunks. It is emulated chunk by chunk, in the
+  order of the rows, as ``dW <- bf16(dW + G_c.T @ X_c)`` starting from zero,
+  with the partial product exact and one round-to-nearest-even per chunk.
+
+No intermediate rounding of the logits or of ``G`` is modelled: the oracle is
+the exact value; the GPU path's bf16 matmul inputs and outputs are covered by
+the tolerances.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from oracle.bf16 import round_to_bf16
+from oracle.ce import count_valid, cross_entropy_rows, reduction_scale
+
+
+def _finish_loss(row_loss_sum_terms, n_valid: int, reduction: str) -> float:
+    total = math.fsum(row_loss_sum_terms)
+    if reduction == "mean":
+        return total / n_valid if n_valid > 0 else math.nan
+    return total
+
+
+def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                         ignore_index: int = -100, reduction: str = "mean",
+                         z_loss_multiplier: float = 0.0,
+                         grad_weight_accum_dtype: str = "fp32",
+                         chunk_size: Optional[int] = None,
+                         block_rows: int = 256):
+    """Loss, grad_inputs and grad_weight of the linear cross-entropy, in fp64.
+
+    ``grad_weight_accum_dtype='fp32'`` returns the exact fp64 gradients (chunking
+    does not change them); ``'weight'`` returns the chunk-by-chunk bf16 emulation
+    of the weight gradient (``chunk_size`` rows per chunk) and the exact
+    ``grad_inputs``. Returns a dict with ``loss``, ``grad_inputs``,
+    ``grad_weight``, ``n_valid``, ``lse`` and ``row_loss``.
+    """
+    BT, D = inputs.shape
+    V = weight.shape[0]
+    n_valid, valid = count_valid(target, ignore_index, V)
+    scale = reduction_scale(n_valid, reduction)
+    X = inputs.to(torch.float64)
+    W = weight.to(torch.float64)
+    dX = torch.zeros((BT, D), dtype=torch.float64)
+    dW = torch.zeros((V, D), dtype=torch.float64)
+    lse = torch.empty(BT, dtype=torch.float64)
+    row_loss = torch.empty(BT, dtype=torch.float64)
+
+    if grad_weight_accum_dtype == "fp32":
+        step = block_rows
+    elif grad_weight_accum_dtype == "weight":
+        if chunk_size is None or chunk_size <= 0:
+            raise ValueError("the weight-dtype emulation needs the chunk size")
+        step = chunk_size
+    else:
+        raise ValueError(f"unknown grad_weight_accum_dtype {grad_weight_accum_dtype!r}")
+
+    for r0 in range(0, BT, step):
+        r1 = min(BT, r0 + step)
+        logits = X[r0:r1] @ W.T                                  # [rows, V]
+        l, rl, G = cross_entropy_rows(logits, target[r0:r1], valid[r0:r1],
+                                      scale, z_loss_multiplier)
+        lse[r0:r1] = l
+        row_loss[r0:r1] = rl
+        dX[r0:r1] = G @ W                                        # [rows, D]
+        if grad_weight_accum_dtype == "fp32":
+            dW.addmm_(G.T, X[r0:r1])                             # exact sum over chunks
+        else:
+            dW = round_to_bf16(dW + G.T @ X[r0:r1])              # rounds between chunks
+    loss = _finish_loss(row_loss.tolist(), n_valid, reduction)
+    return {"loss": loss, "grad_inputs": dX, "grad_weight": dW, "n_valid": n_valid,
+            "lse": lse, "row_loss": row_loss}
+
+
+def linear_cross_entropy_sampled(inputs: torch.Tensor, weight: torch.Tensor,
+                                 target: torch.Tensor, rows: Sequence[int],
+                                 vocab_rows: Sequence[int], ignore_index: int = -100,
+                                 reduction: str = "mean", z_loss_multiplier: float = 0.0,
+                                 block_rows: int = 512):
+    """Exact fp64 loss plus selected rows of grad_inputs and of grad_weight.
+
+    The same definition as ``linear_cross_entropy`` (fp32-accumulation mode),
+    evaluated only where asked so that it stays affordable at full sizes: the
+    loss needs every row's lse; ``grad_inputs[r] = G[r] @ weight`` needs row r of
+    G; ``grad_weight[v] = G[:, v] @ inputs`` needs column v of G for all rows.
+    """
+    BT, D = inputs.shape
+    V = weight.shape[0]
+    n_valid, valid = count_valid(target, ignore_index, V)
+    scale = reduction_scale(n_valid, reduction)
+    W = weight.to(torch.float64)
+    rows_t = torch.as_tensor(list(rows), dtype=torch.int64)
+    cols_t = torch.as_tensor(list(vocab_rows), dtype=torch.int64)
+    dX_rows = torch.zeros((len(rows_t), D), dtype=torch.float64)
+    dW_rows = torch.zeros((len(cols_t), D), dtype=torch.float64)
+    row_loss = torch.empty(BT, dtype=torch.float64)
+    z = z_loss_multiplier
+    for r0 in range(0, BT, block_rows):
+        r1 = min(BT, r0 + block_rows)
+        Xb = inputs[r0:r1].to(torch.float64)
+        logits = Xb @ W.T
+        lse, rl, _ = cross_entropy_rows(logits, target[r0:r1], valid[r0:r1], scale, z,
+                                        want_grad=False)
+        row_loss[r0:r1] = rl
+        # column block of G for the sampled vocabulary rows: scale*((1+2z lse) p - onehot)
+        pc = torch.exp(logits[:, cols_t] - lse.unsqueeze(1)) * (1.0 + 2.0 * z * lse).unsqueeze(1)
+        tb = target[r0:r1].to(torch.int64)
+        pc -= (tb.unsqueeze(1) == cols_t.unsqueeze(0)).to(torch.float64)
+        pc *= scale
+        pc[~valid[r0:r1]] = 0.0
+        dW_rows += pc.T @ Xb
+        # full rows of G for the sampled token rows that fall in this block
+        sel = ((rows_t >= r0) & (rows_t < r1)).nonzero().flatten()
+        if len(sel):
+            loc = rows_t[sel] - r0
+            _, _, G = cross_entropy_rows(logits[loc], tb[loc], valid[r0:r1][loc], scale, z)
+            dX_rows[sel] = G @ W
+    loss = _finish_loss(row_loss.tolist(), n_valid, reduction)
+    return {"loss": loss, "grad_inputs_rows": dX_rows, "grad_weight_rows": dW_rows,
+            "n_valid": n_valid, "row_loss": row_loss}
