@@ -1,0 +1,177 @@
+/*
+ * lmx.h -- C ABI of liblmx.so, large-vocabulary cross-entropy on MI355X (gfx950).
+ *
+ * Two operations, both following the greyhound functional API page:
+ *
+ *   ce_fwd_bwd  -- cross-entropy over materialized logits [B, V]: the reduced
+ *                  loss and the logits gradient in one streaming pass
+ *                  (page entry "cross_entropy": signature, Parameters, Returns).
+ *   linear_ce   -- chunked linear cross-entropy: logits = inputs @ weight.T in
+ *                  row chunks, the same loss and logits gradient per chunk, and
+ *                  grad_inputs / grad_weight accumulated chunk by chunk without
+ *                  materializing the full logits (page entries
+ *                  "chunked_linear_loss" and "chunked_linear_cross_entropy").
+ *
+ * Common conventions
+ * ------------------
+ * - Every pointer argument, except the host-side `workspace_bytes` values, is a
+ *   DEVICE pointer on the current HIP device. Tensors are dense row-major.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *   call only enqueues work on that stream: it never allocates, frees or
+ *   synchronizes, and its outputs are valid once the stream reaches that point.
+ * - The caller owns every buffer, including `workspace`, which must hold at
+ *   least the byte count returned by the matching *_workspace_bytes query and
+ *   be 256-byte aligned. Its contents on entry do not matter; calls that
+ *   overlap in time must not share a workspace.
+ * - Return value: LMX_OK (0) when the work was enqueued, or a negative status
+ *   for an error found on the host; on such an error nothing is enqueued.
+ *   lmx_status_string() names a status.
+ * - Rows whose target equals ignore_index contribute neither loss nor
+ *   gradient (their gradient rows are written as zeros). A valid target
+ *   outside [0, V) breaks the page's precondition; the device sets
+ *   *bad_target = 1 and treats that row as ignored (not counted in N).
+ * - reduction LMX_MEAN divides by N, the number of valid rows of the whole
+ *   call (N = 0 gives a NaN loss and zero gradients); LMX_SUM does not divide.
+ * - The z-loss adds z_loss_multiplier * lse^2 per valid row inside the
+ *   reduction, lse being the natural-log log-sum-exp of the row's logits.
+ * - Arithmetic: fp32 accumulation everywhere; gradients are stored in the
+ *   dtype of the tensor they belong to, rounded to nearest even; the loss is
+ *   an fp32 scalar. The loss is reduced in a fixed order, so repeated calls on
+ *   the same inputs give bitwise-identical results.
+ */
+#ifndef LMX_H_
+#define LMX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the ABI are the only ones the library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define LMX_API __attribute__((visibility("default")))
+#else
+#define LMX_API
+#endif
+
+/* Element type of logits / inputs / weight and of their gradients. */
+typedef enum { LMX_F32 = 0, LMX_BF16 = 1 } lmx_dtype;
+
+/* The page's reduction literal: 'mean' or 'sum' (no 'none'). */
+typedef enum { LMX_MEAN = 0, LMX_SUM = 1 } lmx_reduction;
+
+/* The page's grad_weight_accum_dtype: 'fp32' (fp32 accumulator, cast once at
+ * the end) or 'weight' (accumulate in the weight dtype, rounding between
+ * chunks). */
+typedef enum { LMX_ACC_F32 = 0, LMX_ACC_WEIGHT = 1 } lmx_accum;
+
+/* Status codes. */
+enum {
+  LMX_OK = 0,
+  LMX_ERR_NULL = -1,        /* a required pointer is NULL */
+  LMX_ERR_SIZE = -2,        /* a size is negative or zero where it must be positive */
+  LMX_ERR_ENUM = -3,        /* unknown dtype / reduction / accumulation value */
+  LMX_ERR_WORKSPACE = -4,   /* workspace too small or not 256-byte aligned */
+  LMX_ERR_ALIAS = -5,       /* an output partially overlaps an input */
+  LMX_ERR_ALIGN = -6,       /* a pointer or leading dimension breaks the alignment rule */
+  LMX_ERR_CHUNK = -7,       /* chunk_size < 0 */
+  LMX_ERR_UNSUPPORTED = -8, /* a valid combination this library does not implement */
+  LMX_ERR_HIP = -9          /* a HIP runtime call failed while enqueuing */
+};
+
+/*
+ * ce_fwd_bwd -- cross-entropy loss and logits gradient from materialized logits.
+ *
+ * Defined by the greyhound functional API page, entry "cross_entropy": logits
+ * [B, V], targets [B] in [0, V), ignore_index, reduction 'mean' | 'sum', and
+ * z_loss_multiplier; it returns the cross-entropy plus the z-loss scaled by z.
+ * Per valid row i:  loss_i = lse_i - x[i, t_i] + z * lse_i^2;
+ * gradient row i:   scale * ((1 + 2 z lse_i) * softmax(x_i) - onehot(t_i)),
+ * scale = 1/N (mean) or 1 (sum). This is the gradient for an upstream
+ * gradient of 1; autograd wrappers multiply it by the upstream scalar.
+ *
+ *   logits        [B, V] of `dtype`, row-major, element-aligned.
+ *   grad_logits   [B, V] of `dtype`, or NULL for the loss alone. It may be
+ *                 exactly `logits` (the raw helper that overwrites the logits
+ *                 with their gradient); any other overlap is LMX_ERR_ALIAS.
+ *                 Its address must equal that of `logits` modulo 16
+ *                 (LMX_ERR_ALIGN otherwise; any two 16-byte aligned buffers do).
+ *   target        [B] int64, 8-byte aligned.
+ *   B             rows, >= 0 (B = 0 writes loss = NaN for mean, 0 for sum).
+ *   V             vocabulary size, 1 <= V < 2^30.
+ *   loss          one fp32 on the device (required).
+ *   n_valid       one int64 on the device: N; may be NULL.
+ *   bad_target    one int32 on the device, set to 1 if a valid target lies
+ *                 outside [0, V), else 0; may be NULL.
+ *   workspace     >= ce_workspace_bytes(B, V, dtype) bytes.
+ */
+LMX_API int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target,
+               int64_t B, int64_t V, int dtype, int64_t ignore_index,
+               int reduction, float z_loss_multiplier,
+               float* loss, int64_t* n_valid, int32_t* bad_target,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ce_fwd_bwd needs for these sizes (0 for invalid sizes). */
+LMX_API size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype);
+
+/*
+ * linear_ce -- chunked linear cross-entropy, loss plus grad_inputs and grad_weight.
+ *
+ * Defined by the greyhound functional API page, entries "chunked_linear_loss"
+ * (row chunks of inputs @ weight.T, a loss and logits gradient per chunk,
+ * gradients accumulated chunk by chunk, chunk_size rows per chunk) and
+ * "chunked_linear_cross_entropy" (the cross-entropy specialization with
+ * ignore_index, reduction, z_loss_multiplier and grad_weight_accum_dtype; bf16
+ * matmuls with fp32 accumulator state). 'mean' divides by the number of valid
+ * tokens of the whole call, not of each chunk.
+ *
+ *   inputs        [BT, D] bf16, row-major, 16-byte aligned; D % 8 == 0.
+ *   weight        [V, D]  bf16, row-major, 16-byte aligned.
+ *   target        [BT] int64.
+ *   dtype         LMX_BF16 (the only one implemented; others give
+ *                 LMX_ERR_UNSUPPORTED).
+ *   chunk_size    rows per chunk; 0 picks a size from a 1 GiB budget for the
+ *                 chunk's logits; < 0 is LMX_ERR_CHUNK.
+ *   accum         LMX_ACC_F32: grad_weight is accumulated in an fp32
+ *                 workspace and rounded once; LMX_ACC_WEIGHT: it is
+ *                 accumulated in grad_weight itself, rounding after each chunk.
+ *   loss          one fp32 on the device.
+ *   grad_inputs   [BT, D] bf16 output, 16-byte aligned.
+ *   grad_weight   [V, D]  bf16 output, 16-byte aligned.
+ *   n_valid, bad_target as for ce_fwd_bwd (may be NULL).
+ *   workspace     >= linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum).
+ * Outputs must not overlap the inputs (LMX_ERR_ALIAS).
+ */
+LMX_API int linear_ce(const void* inputs, const void* weight, const int64_t* target,
+              int64_t BT, int64_t D, int64_t V, int dtype,
+              int64_t ignore_index, int reduction, float z_loss_multiplier,
+              int64_t chunk_size, int accum,
+              float* loss, void* grad_inputs, void* grad_weight,
+              int64_t* n_valid, int32_t* bad_target,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes linear_ce needs (0 for invalid arguments). */
+LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
+                                 int64_t chunk_size, int accum);
+
+/* Rows per chunk that linear_ce uses for this chunk_size argument (resolves 0). */
+LMX_API int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size);
+
+/* Human-readable name of a status code (static storage). */
+LMX_API const char* lmx_status_string(int status);
+
+/*
+ * lmx_copy -- plain streaming copy of `bytes` bytes from src to dst on `stream`
+ * (device pointers, 16-byte aligned, non-overlapping). A measurement aid: it is
+ * the copy kernel of known size against which hardware byte counters and the
+ * practical bandwidth ceiling are calibrated. Not part of either operation.
+ */
+LMX_API int lmx_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMX_H_ */

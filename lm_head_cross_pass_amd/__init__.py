@@ -1,0 +1,8 @@
+"""MI355X-native large-vocabulary cross-entropy.
+
+The computation lives in ``liblmx.so`` (hand-written HIP kernels for gfx950,
+C ABI in ``include/lmx.h``); this package is its ctypes binding (``_lib``) and
+the PyTorch-facing functions (``functional``).
+"""
+from lm_head_cross_pass_amd.functional import (  # noqa: F401
+    ce_fwd_bwd, cross_entropy, cross_entropy_, linear_ce, linear_cross_entropy)

@@ -1,0 +1,119 @@
+"""ctypes binding of liblmx.so: the C ABI of ``include/lmx.h``, one Python
+function per C entry point with the same name and argument order.
+
+Arguments are plain integers (device addresses, sizes, enum values) and the
+HIP stream handle; this module only marshals them. Loading fails loudly when
+the library has not been built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblmx.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lmx.h")
+
+# enums of lmx.h
+LMX_F32, LMX_BF16 = 0, 1
+LMX_MEAN, LMX_SUM = 0, 1
+LMX_ACC_F32, LMX_ACC_WEIGHT = 0, 1
+
+STATUS = {
+    0: "LMX_OK", -1: "LMX_ERR_NULL", -2: "LMX_ERR_SIZE", -3: "LMX_ERR_ENUM",
+    -4: "LMX_ERR_WORKSPACE", -5: "LMX_ERR_ALIAS", -6: "LMX_ERR_ALIGN",
+    -7: "LMX_ERR_CHUNK", -8: "LMX_ERR_UNSUPPORTED", -9: "LMX_ERR_HIP",
+}
+for _code, _name in STATUS.items():
+    globals()[_name] = _code
+
+_vp, _i64, _i32, _sz, _f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                              ctypes.c_size_t, ctypes.c_float)
+
+_SIGNATURES = {
+    "ce_fwd_bwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i64, _i32, _f32,
+                          _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ce_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "linear_ce": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _f32,
+                         _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "linear_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32]),
+    "linear_ce_chunk_rows": (_i64, [_i64, _i64, _i64]),
+    "lmx_status_string": (ctypes.c_char_p, [_i32]),
+    "lmx_copy": (_i32, [_vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class LmxError(RuntimeError):
+    """A liblmx.so entry point returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m lm_head_cross_pass_amd.build` "
+                "(or __graft_entry__.build()). There is no CPU fallback.")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions declared in lmx.h (for export checks)."""
+    text = open(path).read()
+    return re.findall(r"LMX_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def status_string(status: int) -> str:
+    return load().lmx_status_string(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise LmxError(fn, status)
+
+
+def ce_fwd_bwd(logits, grad_logits, target, B, V, dtype, ignore_index, reduction,
+               z_loss_multiplier, loss, n_valid, bad_target, workspace, workspace_bytes,
+               stream) -> int:
+    return load().ce_fwd_bwd(logits, grad_logits, target, B, V, dtype, ignore_index,
+                             reduction, z_loss_multiplier, loss, n_valid, bad_target,
+                             workspace, workspace_bytes, stream)
+
+
+def ce_workspace_bytes(B, V, dtype) -> int:
+    return load().ce_workspace_bytes(B, V, dtype)
+
+
+def linear_ce(inputs, weight, target, BT, D, V, dtype, ignore_index, reduction,
+              z_loss_multiplier, chunk_size, accum, loss, grad_inputs, grad_weight,
+              n_valid, bad_target, workspace, workspace_bytes, stream) -> int:
+    return load().linear_ce(inputs, weight, target, BT, D, V, dtype, ignore_index, reduction,
+                            z_loss_multiplier, chunk_size, accum, loss, grad_inputs,
+                            grad_weight, n_valid, bad_target, workspace, workspace_bytes,
+                            stream)
+
+
+def linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum) -> int:
+    return load().linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum)
+
+
+def linear_ce_chunk_rows(BT, V, chunk_size) -> int:
+    return load().linear_ce_chunk_rows(BT, V, chunk_size)
+
+
+def lmx_copy(src, dst, nbytes, stream) -> int:
+    return load().lmx_copy(src, dst, nbytes, stream)

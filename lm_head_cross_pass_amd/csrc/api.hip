@@ -1,0 +1,179 @@
+// The C ABI of liblmx.so: argument checks, workspace carving, then the enqueue
+// functions of the kernel files. Every check here runs on the host before any
+// HIP call, so an invalid call returns a status without touching the device.
+#include <limits.h>
+
+#include "internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool mul_fits(int64_t a, int64_t b, int64_t c) {
+  if (a < 0 || b < 0 || c < 0) return false;
+  if (a == 0 || b == 0 || c == 0) return true;
+  return a <= INT64_MAX / b && a * b <= INT64_MAX / c;
+}
+
+}  // namespace
+
+namespace lmx {
+
+CeWorkspace ce_workspace_layout(int64_t B) {
+  CeWorkspace w;
+  w.n_valid_off = 0;
+  w.row_loss_off = kAlign;
+  w.total = w.row_loss_off + round_up(static_cast<size_t>(B > 0 ? B : 1) * sizeof(float), kAlign);
+  return w;
+}
+
+}  // namespace lmx
+
+extern "C" {
+
+const char* lmx_status_string(int status) {
+  switch (status) {
+    case LMX_OK: return "ok";
+    case LMX_ERR_NULL: return "a required pointer is NULL";
+    case LMX_ERR_SIZE: return "a size is out of range";
+    case LMX_ERR_ENUM: return "unknown dtype, reduction or accumulation value";
+    case LMX_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case LMX_ERR_ALIAS: return "an output overlaps an input";
+    case LMX_ERR_ALIGN: return "a pointer or leading dimension breaks the alignment rule";
+    case LMX_ERR_CHUNK: return "chunk_size is negative";
+    case LMX_ERR_UNSUPPORTED: return "combination not implemented";
+    case LMX_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype) {
+  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30) || (dtype != LMX_F32 && dtype != LMX_BF16)) return 0;
+  return lmx::ce_workspace_layout(B).total;
+}
+
+int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int64_t B,
+               int64_t V, int dtype, int64_t ignore_index, int reduction,
+               float z_loss_multiplier, float* loss, int64_t* n_valid, int32_t* bad_target,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (loss == nullptr || workspace == nullptr) return LMX_ERR_NULL;
+  if (B > 0 && (logits == nullptr || target == nullptr)) return LMX_ERR_NULL;
+  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30)) return LMX_ERR_SIZE;
+  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
+  const int eb = dtype == LMX_BF16 ? 2 : 4;
+  if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
+  const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
+  const uintptr_t pl = reinterpret_cast<uintptr_t>(logits);
+  const uintptr_t pg = reinterpret_cast<uintptr_t>(grad_logits);
+  if (pl % eb != 0 || reinterpret_cast<uintptr_t>(target) % 8 != 0) return LMX_ERR_ALIGN;
+  if (grad_logits != nullptr && (pg % 16) != (pl % 16)) return LMX_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return LMX_ERR_WORKSPACE;
+  if (grad_logits != nullptr && grad_logits != logits &&
+      overlaps(logits, bytes, grad_logits, bytes))
+    return LMX_ERR_ALIAS;
+  if (grad_logits != nullptr && overlaps(grad_logits, bytes, target, B * 8)) return LMX_ERR_ALIAS;
+  const lmx::CeWorkspace wl = lmx::ce_workspace_layout(B);
+  if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  lmx::CeParams p;
+  p.logits = logits;
+  p.grad = grad_logits;
+  p.target = target;
+  p.B = B;
+  p.V = V;
+  p.ignore_index = ignore_index;
+  p.z = z_loss_multiplier;
+  p.reduction = reduction;
+  p.n_valid_ws = reinterpret_cast<int64_t*>(ws + wl.n_valid_off);
+  p.row_loss = reinterpret_cast<float*>(ws + wl.row_loss_off);
+  p.loss = loss;
+  p.n_valid_user = n_valid;
+  p.bad_user = bad_target;
+  return lmx::ce_enqueue(p, dtype, static_cast<hipStream_t>(stream));
+}
+
+int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size) {
+  if (BT < 0 || V <= 0 || chunk_size < 0) return 0;
+  return lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+}
+
+size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
+                                 int64_t chunk_size, int accum) {
+  if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0) return 0;
+  if (dtype != LMX_BF16) return 0;
+  if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return 0;
+  const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+  return lmx::linear_ce_workspace_layout(BT, D, V, c, accum).total;
+}
+
+int linear_ce(const void* inputs, const void* weight, const int64_t* target, int64_t BT,
+              int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction,
+              float z_loss_multiplier, int64_t chunk_size, int accum, float* loss,
+              void* grad_inputs, void* grad_weight, int64_t* n_valid, int32_t* bad_target,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (weight == nullptr || loss == nullptr || grad_weight == nullptr || workspace == nullptr)
+    return LMX_ERR_NULL;
+  if (BT > 0 && (inputs == nullptr || target == nullptr || grad_inputs == nullptr))
+    return LMX_ERR_NULL;
+  if (BT < 0 || D <= 0 || V <= 0) return LMX_ERR_SIZE;
+  if (chunk_size < 0) return LMX_ERR_CHUNK;
+  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
+  if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return LMX_ERR_ENUM;
+  if (dtype != LMX_BF16) return LMX_ERR_UNSUPPORTED;
+  if (!mul_fits(BT, D, 2) || !mul_fits(V, D, 4) || !mul_fits(BT, V, 2)) return LMX_ERR_SIZE;
+  if (D % 8 != 0) return LMX_ERR_ALIGN;
+  for (const void* q : {inputs, weight, static_cast<const void*>(grad_inputs),
+                        static_cast<const void*>(grad_weight)}) {
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return LMX_ERR_ALIGN;
+  }
+  if (reinterpret_cast<uintptr_t>(target) % 8 != 0) return LMX_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return LMX_ERR_WORKSPACE;
+  const size_t xb = static_cast<size_t>(BT) * D * 2, wb = static_cast<size_t>(V) * D * 2;
+  if (overlaps(grad_inputs, xb, inputs, xb) || overlaps(grad_inputs, xb, weight, wb) ||
+      overlaps(grad_weight, wb, inputs, xb) || overlaps(grad_weight, wb, weight, wb) ||
+      overlaps(grad_inputs, xb, grad_weight, wb) || overlaps(grad_inputs, xb, target, BT * 8) ||
+      overlaps(grad_weight, wb, target, BT * 8))
+    return LMX_ERR_ALIAS;
+  const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+  const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum);
+  if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
+  lmx::LinearCeParams p;
+  p.x = static_cast<const uint16_t*>(inputs);
+  p.w = static_cast<const uint16_t*>(weight);
+  p.target = target;
+  p.BT = BT;
+  p.D = D;
+  p.V = V;
+  p.ignore_index = ignore_index;
+  p.z = z_loss_multiplier;
+  p.reduction = reduction;
+  p.chunk = c;
+  p.accum = accum;
+  p.loss = loss;
+  p.grad_x = static_cast<uint16_t*>(grad_inputs);
+  p.grad_w = static_cast<uint16_t*>(grad_weight);
+  p.n_valid_user = n_valid;
+  p.bad_user = bad_target;
+  return lmx::linear_ce_enqueue(p, workspace, static_cast<hipStream_t>(stream));
+}
+
+int lmx_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return LMX_OK;
+  if (src == nullptr || dst == nullptr) return LMX_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return LMX_ERR_ALIGN;
+  if (overlaps(src, bytes, dst, bytes)) return LMX_ERR_ALIAS;
+  return lmx::copy_enqueue(src, dst, bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

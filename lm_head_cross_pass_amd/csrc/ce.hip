@@ -1,0 +1,492 @@
+// Cross-entropy loss and logits gradient over materialized logits [B, V].
+//
+// Method (greyhound functional API page, "cross_entropy"; online log-sum-exp as
+// on the same page's "selective_log_softmax" entry): per valid row, one read
+// sweep finds the row max and the sum of exp(x - max), giving
+// lse = max + log(sum); the row loss is lse - x[t] + z lse^2; a second sweep
+// writes scale * ((1 + 2 z lse) exp(x - lse) - onehot(t)). Ignored rows are
+// only written (zeros).
+//
+// MI355X layout of the work:
+// * one workgroup owns one row at a time and keeps the whole row in VGPRs
+//   between the two sweeps, so the logits are read from HBM exactly once and
+//   the gradient is written exactly once (a 128256-wide bf16 row is 250.5 KiB:
+//   1024 threads x 16 chunks x 16 B);
+// * rows are streamed in 16-byte chunks aligned to the buffer, so rows whose
+//   byte length is not a multiple of 16 (V = 50257 in bf16) still use 128-bit
+//   loads and stores; the partial chunk at each end of a row is masked with
+//   -inf on load and written element by element;
+// * the workgroup count is the number resident on the chip, and each
+//   workgroup walks rows blockIdx, blockIdx + gridDim, ...;
+// * rows too wide for the register file fall back to a streaming kernel that
+//   reads the row twice (the second read usually hits L2 / MALL).
+#include "internal.h"
+
+namespace lmx {
+
+namespace {
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  static constexpr uint32_t kNegInfBits = 0xff800000u;
+  __device__ static void unpack(const u32x4& c, float* x) {
+    x[0] = __uint_as_float(c.x); x[1] = __uint_as_float(c.y);
+    x[2] = __uint_as_float(c.z); x[3] = __uint_as_float(c.w);
+  }
+  __device__ static u32x4 pack(const float* g) {
+    return u32x4{__float_as_uint(g[0]), __float_as_uint(g[1]),
+                 __float_as_uint(g[2]), __float_as_uint(g[3])};
+  }
+  __device__ static float load_one(uintptr_t addr) {
+    return *reinterpret_cast<const float*>(addr);
+  }
+  __device__ static void store_one(__amdgpu_buffer_rsrc_t r, int off, float g) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), r, off, 0, 0);
+  }
+  // Element e of a chunk set to -inf.
+  __device__ static void set_neg_inf(u32x4& c, int e) { c[e] = kNegInfBits; }
+};
+
+template <> struct Elem<uint16_t> {  // bf16 stored as raw 16-bit patterns
+  static constexpr int kPerChunk = 8;
+  __device__ static void unpack(const u32x4& c, float* x) {
+    x[0] = bf16_lo(c.x); x[1] = bf16_hi(c.x); x[2] = bf16_lo(c.y); x[3] = bf16_hi(c.y);
+    x[4] = bf16_lo(c.z); x[5] = bf16_hi(c.z); x[6] = bf16_lo(c.w); x[7] = bf16_hi(c.w);
+  }
+  __device__ static u32x4 pack(const float* g) {
+    return u32x4{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
+                 pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
+  }
+  __device__ static float load_one(uintptr_t addr) {
+    return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(addr));
+  }
+  __device__ static void store_one(__amdgpu_buffer_rsrc_t r, int off, float g) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(g), r, off, 0, 0);
+  }
+  __device__ static void set_neg_inf(u32x4& c, int e) {
+    const uint32_t w = c[e >> 1];
+    c[e >> 1] = (e & 1) ? ((w & 0x0000ffffu) | 0xff800000u) : ((w & 0xffff0000u) | 0x0000ff80u);
+  }
+};
+
+// Makes the compiler forget what it knows about a register-resident chunk, so
+// each sweep re-widens the packed data instead of keeping a widened copy of the
+// whole row alive (which would not fit the register file).
+__device__ __forceinline__ void launder(u32x4& c) { asm volatile("" : "+v"(c)); }
+
+// exp(x - m) * 2^-extra, evaluated as a base-2 exponential. fp32 logits take
+// the difference x - m first (exact when x is near the max, where the
+// probabilities are large), which keeps the gradient within a few fp32 ulps
+// of the exact value; bf16 logits fold everything into one fma, whose
+// rounding is far below the bf16 output's.
+template <typename T>
+__device__ __forceinline__ float shifted_exp2(float x, float m, float extra, float comb) {
+  if constexpr (sizeof(T) == 4) {
+    return exp2_fast(__builtin_fmaf(x - m, kLog2e, -extra));
+  } else {
+    return exp2_fast(__builtin_fmaf(x, kLog2e, -comb));   // comb = m * log2(e) + extra
+  }
+}
+
+// Buffer descriptor word 3 for untyped (raw) buffer access on CDNA.
+constexpr int kRawBufferFlags = 0x00020000;
+// Cache policy of the streaming loads and stores: non-temporal.
+constexpr int kStreamAux = 2;
+
+// One row as a buffer resource over the 16-byte chunks it touches. Loads past
+// the end return zeros and stores past the end are dropped by the hardware, so
+// per-chunk offsets are 32-bit and need no range checks.
+struct RowView {
+  __amdgpu_buffer_rsrc_t in, out;
+  uintptr_t first;   // address of the chunk holding the row's first element
+  int lead;          // elements of that chunk that precede the row
+  int nch;           // chunks touched by the row
+};
+
+template <typename T>
+__device__ __forceinline__ RowView row_view(uintptr_t base, uintptr_t gbase, int64_t row,
+                                            int64_t V) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  RowView r;
+  const uintptr_t a0 = base + static_cast<uintptr_t>(row) * static_cast<uintptr_t>(V) * sizeof(T);
+  r.first = a0 & ~static_cast<uintptr_t>(15);
+  r.lead = static_cast<int>((a0 - r.first) / sizeof(T));
+  r.nch = static_cast<int>((r.lead + V + EPC - 1) / EPC);
+  r.in = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(r.first), 0, r.nch * 16,
+                                           kRawBufferFlags);
+  r.out = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(gbase + (r.first - base)), 0,
+                                            r.nch * 16, kRawBufferFlags);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 load_chunk(const RowView& r, int ci) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r.in, ci * 16, 0, kStreamAux);
+}
+
+// Sets the elements of chunk ci that are not part of the row to -inf (the
+// partial chunks at both ends, and chunks past the end). Column arithmetic is
+// 32-bit: the host rejects V >= 2^30.
+template <typename T>
+__device__ __forceinline__ void mask_edges(u32x4& c, int ci, const RowView& r, int V) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  if (ci == 0 || ci >= r.nch - 1) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const int j = ci * EPC + e - r.lead;
+      if (j < 0 || j >= V) Elem<T>::set_neg_inf(c, e);
+    }
+  }
+}
+
+// Stores gradient chunk ci: one 128-bit store for an interior chunk, element
+// stores for the partial chunks at the row's ends. Chunks past the end fall
+// outside the buffer resource and are dropped.
+template <typename T>
+__device__ __forceinline__ void store_chunk(const RowView& r, int ci, int V, const float* vals) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const bool partial = (ci == 0 && r.lead != 0) ||
+                       (ci == r.nch - 1 && (r.lead + V) % EPC != 0);
+  if (!partial) {
+    __builtin_amdgcn_raw_buffer_store_b128(Elem<T>::pack(vals), r.out, ci * 16, 0, kStreamAux);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const int j = ci * EPC + e - r.lead;
+      if (j >= 0 && j < V) Elem<T>::store_one(r.out, ci * 16 + e * static_cast<int>(sizeof(T)), vals[e]);
+    }
+  }
+}
+
+__device__ __forceinline__ float reduction_scale(const CeParams& p) {
+  const int64_t n = *p.n_valid_ws;
+  return p.reduction == LMX_MEAN ? 1.0f / static_cast<float>(n) : 1.0f;
+}
+
+__device__ __forceinline__ bool row_is_valid(int64_t t, const CeParams& p) {
+  return t != p.ignore_index && t >= 0 && t < p.V;
+}
+
+// Writes a zero gradient row (ignored rows); nothing is read.
+template <typename T, int THREADS>
+__device__ __forceinline__ void zero_row(const CeParams& p, int64_t row) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const uintptr_t gb = reinterpret_cast<uintptr_t>(p.grad);
+  const RowView r = row_view<T>(gb, gb, row, p.V);
+  float z[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) z[e] = 0.f;
+  for (int ci = threadIdx.x; ci < r.nch; ci += THREADS) store_chunk<T>(r, ci, static_cast<int>(p.V), z);
+}
+
+// Block-wide combine of per-thread (max, sum) pairs; every thread gets the result.
+template <int THREADS>
+__device__ __forceinline__ void block_lse(float& m, float& s, float* sm, float* ss) {
+  constexpr int W = THREADS / 64;
+  wave_lse_combine(m, s);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[w] = m; ss[w] = s; }
+  __syncthreads();
+  m = sm[0];
+  s = ss[0];
+#pragma unroll
+  for (int i = 1; i < W; ++i) lse_combine(m, s, sm[i], ss[i]);
+}
+
+// ------------------------------------------------------------------ kernels
+
+// N = number of valid rows, and the out-of-range flag. One workgroup, so the
+// count needs no atomics and no zeroed memory.
+__global__ __launch_bounds__(1024) void ce_count_kernel(const int64_t* target, int64_t B,
+                                                        int64_t V, int64_t ignore_index,
+                                                        int64_t* n_ws, int64_t* n_user,
+                                                        int32_t* bad_user) {
+  __shared__ int64_t sn[16];
+  __shared__ int sb[16];
+  int64_t n = 0;
+  int bad = 0;
+  for (int64_t i = threadIdx.x; i < B; i += 1024) {
+    const int64_t t = target[i];
+    if (t != ignore_index) {
+      if (t >= 0 && t < V) ++n; else bad = 1;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    n += __shfl_xor(n, off, 64);
+    bad |= __shfl_xor(bad, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) { sn[threadIdx.x >> 6] = n; sb[threadIdx.x >> 6] = bad; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t tn = 0;
+    int tb = 0;
+    for (int i = 0; i < 16; ++i) { tn += sn[i]; tb |= sb[i]; }
+    *n_ws = tn;
+    if (n_user) *n_user = tn;
+    if (bad_user) *bad_user = tb;
+  }
+}
+
+// Register-resident rows: THREADS x CPT chunks of 16 B must cover a row.
+template <typename T, int THREADS, int CPT>
+__global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  constexpr int W = THREADS / 64;
+  __shared__ float sm[2][W], ss[2][W];
+  __shared__ float sxt[2];
+  const int tid = threadIdx.x;
+  const float scale = reduction_scale(p);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p.logits);
+  const bool want_grad = p.grad != nullptr;
+  const uintptr_t gbase = want_grad ? reinterpret_cast<uintptr_t>(p.grad) : base;
+  const int V = static_cast<int>(p.V);
+  int par = 0;  // LDS slot parity; flips once per valid row (each has one barrier)
+  for (int64_t row = blockIdx.x; row < p.B; row += gridDim.x) {
+    const int64_t t = p.target[row];
+    if (!row_is_valid(t, p)) {
+      if (tid == 0) p.row_loss[row] = 0.f;
+      if (want_grad) zero_row<T, THREADS>(p, row);
+      continue;
+    }
+    const RowView r = row_view<T>(base, gbase, row, p.V);
+    if (tid == 0) {
+      sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.V + t) * sizeof(T));
+    }
+    u32x4 d[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int ci = tid + k * THREADS;
+      d[k] = load_chunk(r, ci);
+      mask_edges<T>(d[k], ci, r, V);
+    }
+    // sweep 1: thread max, then the thread's sum of exp(x - max)
+    float m = -kInf;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      float x[EPC];
+      Elem<T>::unpack(d[k], x);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) m = fmaxf(m, x[e]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) launder(d[k]);
+    if (m != -kInf) {
+      const float mL = m * kLog2e;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float x[EPC];
+        Elem<T>::unpack(d[k], x);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s += shifted_exp2<T>(x[e], m, 0.f, mL);
+      }
+    }
+    block_lse<THREADS>(m, s, sm[par], ss[par]);
+    const float log2s = log2_fast(s);          // lse = m + ln(s), m the row max
+    const float lse = m + log2s * kLn2;
+    const float xt = sxt[par];
+    par ^= 1;
+    if (tid == 0) p.row_loss[row] = (m - xt) + log2s * kLn2 + p.z * lse * lse;
+    if (!want_grad) continue;
+    // sweep 2: gradient from the registers
+    const float c = scale * (1.f + 2.f * p.z * lse);
+    const int tpos = r.lead + static_cast<int>(t);
+    const int ct = tpos / EPC;
+    const int et = tpos % EPC;
+    const bool fold = c > 0.f && c < kInf;   // c folded into the exponent
+    const float extra = fold ? log2s - log2_fast(c) : log2s;
+    const float comb = m * kLog2e + extra;
+    const float mul = fold ? 1.f : c;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) launder(d[k]);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int ci = tid + k * THREADS;
+      float x[EPC];
+      Elem<T>::unpack(d[k], x);
+      float gv[EPC];
+      if (fold) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) gv[e] = shifted_exp2<T>(x[e], m, extra, comb);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) gv[e] = mul * shifted_exp2<T>(x[e], m, extra, comb);
+      }
+      if (ci == ct) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) if (e == et) gv[e] -= scale;
+      }
+      store_chunk<T>(r, ci, V, gv);
+    }
+  }
+}
+
+// Rows of any width: two read sweeps with an online max / sum per thread.
+template <typename T, int THREADS>
+__global__ __launch_bounds__(THREADS) void ce_rows_stream_kernel(CeParams p) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  constexpr int W = THREADS / 64;
+  __shared__ float sm[2][W], ss[2][W];
+  __shared__ float sxt[2];
+  const int tid = threadIdx.x;
+  const float scale = reduction_scale(p);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p.logits);
+  const bool want_grad = p.grad != nullptr;
+  const uintptr_t gbase = want_grad ? reinterpret_cast<uintptr_t>(p.grad) : base;
+  const int V = static_cast<int>(p.V);
+  int par = 0;
+  for (int64_t row = blockIdx.x; row < p.B; row += gridDim.x) {
+    const int64_t t = p.target[row];
+    if (!row_is_valid(t, p)) {
+      if (tid == 0) p.row_loss[row] = 0.f;
+      if (want_grad) zero_row<T, THREADS>(p, row);
+      continue;
+    }
+    const RowView r = row_view<T>(base, gbase, row, p.V);
+    if (tid == 0) {
+      sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.V + t) * sizeof(T));
+    }
+    float m = -kInf, s = 0.f;
+    for (int ci = tid; ci < r.nch; ci += THREADS) {
+      u32x4 c = load_chunk(r, ci);
+      mask_edges<T>(c, ci, r, V);
+      float x[EPC];
+      Elem<T>::unpack(c, x);
+      float cm = x[0];
+#pragma unroll
+      for (int e = 1; e < EPC; ++e) cm = fmaxf(cm, x[e]);
+      if (cm > m) {
+        s = (m == -kInf) ? 0.f : s * exp2_fast((m - cm) * kLog2e);
+        m = cm;
+      }
+      if (m != -kInf) {
+        const float mL = m * kLog2e;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s += shifted_exp2<T>(x[e], m, 0.f, mL);
+      }
+    }
+    block_lse<THREADS>(m, s, sm[par], ss[par]);
+    const float log2s = log2_fast(s);
+    const float lse = m + log2s * kLn2;
+    const float xt = sxt[par];
+    par ^= 1;
+    if (tid == 0) p.row_loss[row] = (m - xt) + log2s * kLn2 + p.z * lse * lse;
+    if (!want_grad) continue;
+    const float c = scale * (1.f + 2.f * p.z * lse);
+    const int tpos = r.lead + static_cast<int>(t);
+    const int ct = tpos / EPC;
+    const int et = tpos % EPC;
+    const float comb = m * kLog2e + log2s;
+    for (int ci = tid; ci < r.nch; ci += THREADS) {
+      u32x4 cch = load_chunk(r, ci);
+      float x[EPC];
+      Elem<T>::unpack(cch, x);
+      float gv[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) gv[e] = c * shifted_exp2<T>(x[e], m, log2s, comb);
+      if (ci == ct) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) if (e == et) gv[e] -= scale;
+      }
+      store_chunk<T>(r, ci, V, gv);
+    }
+  }
+}
+
+// Fixed-order sum of the row losses (fp64 partial sums), then / N for mean.
+__global__ __launch_bounds__(1024) void ce_finish_kernel(const float* row_loss, int64_t B,
+                                                         const int64_t* n_ws, int reduction,
+                                                         float* loss) {
+  __shared__ double sd[16];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < B; i += 1024) acc += static_cast<double>(row_loss[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) sd[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < 16; ++i) tot += sd[i];
+    const double n = static_cast<double>(*n_ws);
+    *loss = static_cast<float>(reduction == LMX_MEAN ? tot / n : tot);
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+struct RowKernel {
+  const void* fn;
+  int threads;
+  int64_t capacity;  // chunks per row that fit; 0 = any (streaming)
+};
+
+template <typename T>
+const RowKernel* row_kernels(int* count) {
+  static const RowKernel k[] = {
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 1>), 256, 256},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 2>), 256, 512},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 4>), 256, 1024},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 8>), 256, 2048},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 16>), 256, 4096},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13>), 512, 6656},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 16>), 512, 8192},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 12>), 1024, 12288},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 16>), 1024, 16384},
+      {reinterpret_cast<const void*>(&ce_rows_stream_kernel<T, 1024>), 1024, 0},
+  };
+  *count = static_cast<int>(sizeof(k) / sizeof(k[0]));
+  return k;
+}
+
+}  // namespace
+
+// Largest number of 16-byte chunks one row of this call touches.
+int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int elem_bytes) {
+  const int64_t epc = 16 / elem_bytes;
+  const int64_t lead0 = static_cast<int64_t>((base & 15u) / elem_bytes);
+  if ((V * elem_bytes) % 16 == 0) return (lead0 + V + epc - 1) / epc;
+  return (epc - 1 + V + epc - 1) / epc;
+}
+
+static int occupancy_grid(const void* fn, int threads, int64_t rows) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
+    return -1;
+  if (per_cu < 1) per_cu = 1;
+  const int64_t resident = static_cast<int64_t>(per_cu) * cus;
+  return static_cast<int>(rows < resident ? rows : resident);
+}
+
+int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
+  hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, p.target, p.B, p.V,
+                     p.ignore_index, p.n_valid_ws, p.n_valid_user, p.bad_user);
+  if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
+  if (p.B > 0) {
+    const int eb = dtype == LMX_BF16 ? 2 : 4;
+    const int64_t need = ce_max_row_chunks(reinterpret_cast<uintptr_t>(p.logits), p.V, eb);
+    int n = 0;
+    const RowKernel* ks = dtype == LMX_BF16 ? row_kernels<uint16_t>(&n) : row_kernels<float>(&n);
+    const RowKernel* pick = &ks[n - 1];
+    for (int i = 0; i < n; ++i) {
+      if (ks[i].capacity == 0 || ks[i].capacity >= need) { pick = &ks[i]; break; }
+    }
+    const int grid = occupancy_grid(pick->fn, pick->threads, p.B);
+    if (grid <= 0) return LMX_ERR_HIP;
+    CeParams pc = p;
+    void* args[] = {&pc};
+    if (hipLaunchKernel(pick->fn, dim3(grid), dim3(pick->threads), args, 0, stream) != hipSuccess)
+      return LMX_ERR_HIP;
+  }
+  hipLaunchKernelGGL(ce_finish_kernel, dim3(1), dim3(1024), 0, stream, p.row_loss, p.B,
+                     p.n_valid_ws, p.reduction, p.loss);
+  if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
+  return LMX_OK;
+}
+
+}  // namespace lmx

@@ -1,0 +1,69 @@
+// Host-side interfaces between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include "common.h"
+
+namespace lmx {
+
+// Arguments of one cross-entropy call, as the kernels see them.
+struct CeParams {
+  const void* logits;       // [B, V]
+  void* grad;               // [B, V] or nullptr (loss only); may equal logits
+  const int64_t* target;    // [B]
+  int64_t B, V;
+  int64_t ignore_index;
+  float z;                  // z_loss_multiplier
+  int reduction;            // LMX_MEAN / LMX_SUM
+  int64_t* n_valid_ws;      // workspace: N (written by the count kernel)
+  float* row_loss;          // workspace: [B] row loss terms
+  float* loss;              // output scalar
+  int64_t* n_valid_user;    // optional output
+  int32_t* bad_user;        // optional output
+};
+
+// Enqueues count -> rows -> finish for one cross-entropy call.
+int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream);
+
+// Largest number of 16-byte chunks any row touches (for kernel selection).
+int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int elem_bytes);
+
+// Workspace layout of ce_fwd_bwd.
+struct CeWorkspace {
+  size_t n_valid_off, row_loss_off, total;
+};
+CeWorkspace ce_workspace_layout(int64_t B);
+
+// Linear cross-entropy.
+struct LinearCeParams {
+  const uint16_t* x;        // [BT, D] bf16
+  const uint16_t* w;        // [V, D] bf16
+  const int64_t* target;    // [BT]
+  int64_t BT, D, V;
+  int64_t ignore_index;
+  float z;
+  int reduction;
+  int64_t chunk;            // rows per chunk (resolved, > 0)
+  int accum;                // LMX_ACC_F32 / LMX_ACC_WEIGHT
+  float* loss;
+  uint16_t* grad_x;         // [BT, D] bf16
+  uint16_t* grad_w;         // [V, D] bf16
+  int64_t* n_valid_user;
+  int32_t* bad_user;
+};
+
+struct LinearCeWorkspace {
+  int64_t ldv;              // padded vocabulary stride of the chunk buffers
+  int64_t ldc;              // padded chunk-row stride of the transposed buffers
+  int64_t ntn;              // vocabulary tiles of the logits GEMM
+  int64_t ksplit;           // K splits of the grad_inputs GEMM
+  size_t n_valid_off, row_loss_off, lse_off, part_off, z_off, gt_off, xt_off, wt_off,
+      dxp_off, dw_off, total;
+};
+LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, int64_t chunk,
+                                             int accum);
+int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size);
+int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream);
+
+int copy_enqueue(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace lmx

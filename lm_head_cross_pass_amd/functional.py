@@ -1,0 +1,181 @@
+"""PyTorch-facing functions over liblmx.so (greyhound functional API page).
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. The functions:
+
+* ``cross_entropy``  -- loss from materialized logits with normal autograd
+  behaviour; the logits are not modified (page entry ``cross_entropy``);
+* ``cross_entropy_`` -- the raw helper: returns the loss and overwrites the
+  logits with their gradient (upstream gradient 1);
+* ``linear_cross_entropy`` -- chunked ``inputs @ weight.T`` cross-entropy with
+  gradients for inputs and weight (page entries ``chunked_linear_loss`` and
+  ``chunked_linear_cross_entropy``; ``chunk_size`` as in the former).
+
+The gradients are produced in the forward call (one pass); backward only
+scales them by the upstream scalar gradient.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from lm_head_cross_pass_amd import _lib
+
+_DTYPES = {torch.float32: _lib.LMX_F32, torch.bfloat16: _lib.LMX_BF16}
+_REDUCTIONS = {"mean": _lib.LMX_MEAN, "sum": _lib.LMX_SUM}
+_ACCUMS = {"fp32": _lib.LMX_ACC_F32, "weight": _lib.LMX_ACC_WEIGHT}
+
+
+def _require_device(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    # the caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def ce_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
+               reduction: str = "mean", z_loss_multiplier: float = 0.0,
+               grad: Optional[torch.Tensor] = None, want_grad: bool = True,
+               in_place: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor],
+                                                torch.Tensor, torch.Tensor]:
+    """One library call: (loss fp32 scalar, grad or None, n_valid int64, bad_target int32).
+
+    ``in_place=True`` writes the gradient over ``logits``; otherwise a gradient
+    buffer is allocated (or ``grad`` is used) when ``want_grad``.
+    """
+    _require_device(logits, "logits")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [B, V] tensor")
+    if logits.dtype not in _DTYPES:
+        raise ValueError(f"unsupported logits dtype {logits.dtype}")
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'sum', not {reduction!r}")
+    B, V = logits.shape
+    target = target.to(device=logits.device, dtype=torch.int64).contiguous()
+    if target.shape != (B,):
+        raise ValueError("target must have shape [B]")
+    dev = logits.device
+    if in_place:
+        grad = logits
+    elif want_grad and grad is None:
+        grad = torch.empty_like(logits)
+    elif not want_grad:
+        grad = None
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    dtype = _DTYPES[logits.dtype]
+    nbytes = _lib.ce_workspace_bytes(B, V, dtype)
+    ws = _workspace(nbytes, dev)
+    with torch.cuda.device(dev):
+        st = _lib.ce_fwd_bwd(logits.data_ptr(), grad.data_ptr() if grad is not None else None,
+                             target.data_ptr(), B, V, dtype, int(ignore_index),
+                             _REDUCTIONS[reduction], float(z_loss_multiplier), loss.data_ptr(),
+                             n_valid.data_ptr(), bad.data_ptr(), ws.data_ptr(), ws.numel(),
+                             _stream_handle(dev))
+    _lib.check("ce_fwd_bwd", st)
+    return loss, grad, n_valid, bad
+
+
+class _CrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, target, ignore_index, reduction, z):
+        loss, grad, _, _ = ce_fwd_bwd(logits.detach(), target, ignore_index, reduction, z,
+                                      want_grad=logits.requires_grad)
+        ctx.save_for_backward(grad if grad is not None else logits.new_empty(0))
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (grad,) = ctx.saved_tensors
+        return grad * grad_out.to(grad.dtype), None, None, None, None
+
+
+def cross_entropy(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
+                  reduction: str = "mean", z_loss_multiplier: float = 0.0) -> torch.Tensor:
+    """Cross-entropy plus z-loss from materialized logits [B, V]; does not mutate logits."""
+    return _CrossEntropy.apply(logits, target, ignore_index, reduction, z_loss_multiplier)
+
+
+def cross_entropy_(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
+                   reduction: str = "mean", z_loss_multiplier: float = 0.0) -> torch.Tensor:
+    """Raw helper: returns the loss and overwrites ``logits`` with d(loss)/d(logits)."""
+    loss, _, _, _ = ce_fwd_bwd(logits, target, ignore_index, reduction, z_loss_multiplier,
+                               in_place=True)
+    return loss
+
+
+def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+              ignore_index: int = -100, reduction: str = "mean",
+              z_loss_multiplier: float = 0.0, chunk_size: Optional[int] = None,
+              grad_weight_accum_dtype: str = "fp32",
+              workspace: Optional[torch.Tensor] = None):
+    """One library call: (loss, grad_inputs, grad_weight, n_valid, bad_target)."""
+    for t, n in ((inputs, "inputs"), (weight, "weight")):
+        _require_device(t, n)
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 2-D tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bfloat16 (the matmuls run in bf16)")
+    BT, D = inputs.shape
+    V, D2 = weight.shape
+    if D2 != D:
+        raise ValueError("inputs [BT, D] and weight [V, D] disagree on D")
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'sum', not {reduction!r}")
+    if grad_weight_accum_dtype not in _ACCUMS:
+        raise ValueError("grad_weight_accum_dtype must be 'fp32' or 'weight'")
+    dev = inputs.device
+    target = target.to(device=dev, dtype=torch.int64).contiguous()
+    if target.shape != (BT,):
+        raise ValueError("target must have shape [BT]")
+    cs = 0 if chunk_size is None else int(chunk_size)
+    acc = _ACCUMS[grad_weight_accum_dtype]
+    nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, _lib.LMX_BF16, cs, acc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    gx = torch.empty_like(inputs)
+    gw = torch.empty_like(weight)
+    with torch.cuda.device(dev):
+        st = _lib.linear_ce(inputs.data_ptr(), weight.data_ptr(), target.data_ptr(), BT, D, V,
+                            _lib.LMX_BF16, int(ignore_index), _REDUCTIONS[reduction],
+                            float(z_loss_multiplier), cs, acc, loss.data_ptr(), gx.data_ptr(),
+                            gw.data_ptr(), n_valid.data_ptr(), bad.data_ptr(),
+                            workspace.data_ptr(), workspace.numel(), _stream_handle(dev))
+    _lib.check("linear_ce", st)
+    return loss, gx, gw, n_valid, bad
+
+
+class _LinearCrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, inputs, weight, target, ignore_index, reduction, z, chunk_size, accum):
+        loss, gx, gw, _, _ = linear_ce(inputs.detach(), weight.detach(), target, ignore_index,
+                                       reduction, z, chunk_size, accum)
+        ctx.save_for_backward(gx, gw)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        gx, gw = ctx.saved_tensors
+        g = grad_out.to(gx.dtype)
+        return gx * g, gw * g, None, None, None, None, None, None
+
+
+def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                         ignore_index: int = -100, reduction: str = "mean",
+                         z_loss_multiplier: float = 0.0, chunk_size: Optional[int] = None,
+                         grad_weight_accum_dtype: str = "fp32") -> torch.Tensor:
+    """Chunked linear cross-entropy with z-loss; gradients flow to inputs and weight."""
+    return _LinearCrossEntropy.apply(inputs, weight, target, ignore_index, reduction,
+                                     z_loss_multiplier, chunk_size, grad_weight_accum_dtype)

@@ -1,0 +1,147 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+``include/lmx.h`` declares, sizes workspaces, and rejects bad arguments with
+the documented status before touching the device.
+
+The argument-check calls pass made-up addresses: the library only does
+arithmetic on them on the host and returns an error status before any HIP
+call, so nothing is ever dereferenced.
+"""
+import os
+
+import pytest
+
+from lm_head_cross_pass_amd import _lib
+
+F32, BF16 = _lib.LMX_F32, _lib.LMX_BF16
+MEAN, SUM = _lib.LMX_MEAN, _lib.LMX_SUM
+A = 1 << 40          # a fake, 256-byte aligned device address
+WS = 1 << 20
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(_lib.LIB_PATH):
+        from lm_head_cross_pass_amd import build
+        build.build()
+    _lib.load()
+
+
+def test_every_declared_function_is_exported():
+    names = _lib.header_functions()
+    assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "linear_ce",
+                          "linear_ce_workspace_bytes", "linear_ce_chunk_rows",
+                          "lmx_status_string", "lmx_copy"}
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True)
+    if out.returncode != 0:
+        pytest.skip("nm not available")
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if " T " in ln}
+    assert exported == set(_lib.header_functions())
+
+
+def test_status_strings():
+    for code in _lib.STATUS:
+        assert _lib.status_string(code)
+    assert _lib.status_string(12345) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert _lib.ce_workspace_bytes(16384, 128256, BF16) >= 16384 * 4
+    assert _lib.ce_workspace_bytes(0, 10, F32) > 0
+    assert _lib.ce_workspace_bytes(-1, 10, F32) == 0
+    assert _lib.ce_workspace_bytes(4, 0, F32) == 0
+    assert _lib.ce_workspace_bytes(4, 10, 7) == 0
+    assert _lib.ce_workspace_bytes(4, 1 << 30, BF16) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 0) > 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, F32, 1024, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, -1, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 5) == 0
+
+
+def test_chunk_rows():
+    assert _lib.linear_ce_chunk_rows(8192, 50257, 1024) == 1024
+    assert _lib.linear_ce_chunk_rows(100, 50257, 1024) == 100
+    c = _lib.linear_ce_chunk_rows(16384, 128256, 0)
+    assert 1 <= c <= 16384
+
+
+def _ce(**kw):
+    args = dict(logits=A, grad=A + (1 << 34), target=A + (2 << 34), B=8, V=1000, dtype=F32,
+                ignore=-100, red=MEAN, z=0.0, loss=A + (3 << 34), n=None, bad=None,
+                ws=A + (4 << 34), wsb=WS, stream=None)
+    args.update(kw)
+    return _lib.ce_fwd_bwd(args["logits"], args["grad"], args["target"], args["B"], args["V"],
+                           args["dtype"], args["ignore"], args["red"], args["z"], args["loss"],
+                           args["n"], args["bad"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(loss=None), _lib.LMX_ERR_NULL),
+    (dict(ws=None), _lib.LMX_ERR_NULL),
+    (dict(logits=None), _lib.LMX_ERR_NULL),
+    (dict(target=None), _lib.LMX_ERR_NULL),
+    (dict(B=-1), _lib.LMX_ERR_SIZE),
+    (dict(V=0), _lib.LMX_ERR_SIZE),
+    (dict(V=1 << 30), _lib.LMX_ERR_SIZE),
+    (dict(B=1 << 62), _lib.LMX_ERR_SIZE),
+    (dict(dtype=2), _lib.LMX_ERR_ENUM),
+    (dict(red=2), _lib.LMX_ERR_ENUM),
+    (dict(logits=A + 2), _lib.LMX_ERR_ALIGN),           # fp32 needs 4-byte alignment
+    (dict(target=A + 4), _lib.LMX_ERR_ALIGN),
+    (dict(grad=A + (1 << 34) + 4), _lib.LMX_ERR_ALIGN), # differs from logits modulo 16
+    (dict(ws=A + 64), _lib.LMX_ERR_WORKSPACE),
+    (dict(wsb=16), _lib.LMX_ERR_WORKSPACE),
+    (dict(grad=A + 4000 * 4 + 16 * 0), _lib.LMX_ERR_ALIAS),  # overlaps logits, not equal
+])
+def test_ce_argument_errors(kw, status):
+    assert _ce(**kw) == status
+
+
+def _lin(**kw):
+    args = dict(x=A, w=A + (1 << 34), t=A + (2 << 34), BT=64, D=64, V=1000, dtype=BF16,
+                ignore=-100, red=MEAN, z=0.0, chunk=16, acc=0, loss=A + (3 << 34),
+                gx=A + (5 << 34), gw=A + (6 << 34), n=None, bad=None, ws=A + (4 << 34),
+                wsb=1 << 40, stream=None)
+    args.update(kw)
+    return _lib.linear_ce(args["x"], args["w"], args["t"], args["BT"], args["D"], args["V"],
+                          args["dtype"], args["ignore"], args["red"], args["z"], args["chunk"],
+                          args["acc"], args["loss"], args["gx"], args["gw"], args["n"],
+                          args["bad"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), _lib.LMX_ERR_NULL),
+    (dict(gw=None), _lib.LMX_ERR_NULL),
+    (dict(x=None), _lib.LMX_ERR_NULL),
+    (dict(BT=-1), _lib.LMX_ERR_SIZE),
+    (dict(D=0), _lib.LMX_ERR_SIZE),
+    (dict(V=0), _lib.LMX_ERR_SIZE),
+    (dict(chunk=-1), _lib.LMX_ERR_CHUNK),
+    (dict(dtype=F32), _lib.LMX_ERR_UNSUPPORTED),
+    (dict(dtype=3), _lib.LMX_ERR_ENUM),
+    (dict(red=5), _lib.LMX_ERR_ENUM),
+    (dict(acc=2), _lib.LMX_ERR_ENUM),
+    (dict(D=60), _lib.LMX_ERR_ALIGN),
+    (dict(x=A + 8), _lib.LMX_ERR_ALIGN),
+    (dict(gw=A + (6 << 34) + 2), _lib.LMX_ERR_ALIGN),
+    (dict(ws=A + 128), _lib.LMX_ERR_WORKSPACE),
+    (dict(wsb=256), _lib.LMX_ERR_WORKSPACE),
+    (dict(gx=A + 64), _lib.LMX_ERR_ALIAS),               # overlaps inputs
+    (dict(gw=A + (1 << 34) + 1024), _lib.LMX_ERR_ALIAS), # overlaps weight
+])
+def test_linear_ce_argument_errors(kw, status):
+    assert _lin(**kw) == status
+
+
+def test_copy_argument_errors():
+    assert _lib.lmx_copy(None, A, 16, None) == _lib.LMX_ERR_NULL
+    assert _lib.lmx_copy(A + 8, A + (1 << 34), 16, None) == _lib.LMX_ERR_ALIGN
+    assert _lib.lmx_copy(A, A + 16, 64, None) == _lib.LMX_ERR_ALIAS
+    assert _lib.lmx_copy(A, A, 0, None) == _lib.LMX_OK

@@ -1,0 +1,226 @@
+"""GPU parity of ce_fwd_bwd against the fp64 oracle (needs an MI355X).
+
+Tolerances (stated with the method's workloads):
+* fp32 logits: loss within 1e-5 relative, gradient within 1e-6 absolute;
+* bf16 logits: loss within 2e-3 relative, gradient within 1e-2 relative
+  Frobenius norm ||g - g*|| / ||g*||, plus an element-wise bound of one bf16
+  rounding on top of the fp32 arithmetic (|g - g*| <= 2^-8 |g*| + 1e-7 scale);
+* the valid-token count N is compared exactly.
+Inputs are the seeded workloads of ``workloads.py``; the oracle computes on the
+same host bit patterns.
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from lm_head_cross_pass_amd import _lib
+from lm_head_cross_pass_amd import functional as F
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _check(logits, target, red, z, got_loss, got_grad, got_n, rows=None, ref=None):
+    if ref is None:
+        ref = oracle.cross_entropy(logits, target, -100, red, z)
+    assert int(got_n) == ref["n_valid"]
+    rl = float(got_loss)
+    if math.isnan(ref["loss"]):
+        assert math.isnan(rl)
+    elif logits.dtype == torch.float32:
+        assert rl == pytest.approx(ref["loss"], rel=1e-5, abs=1e-30)
+    else:
+        assert rl == pytest.approx(ref["loss"], rel=2e-3, abs=1e-30)
+    if got_grad is None:
+        return
+    g = got_grad.double().cpu()
+    gs = ref["grad"]
+    if rows is not None:
+        g = g[rows]
+    if logits.dtype == torch.float32:
+        assert float((g - gs).abs().max()) <= 1e-6
+    else:
+        n = float(gs.norm())
+        if n > 0:
+            assert float((g - gs).norm()) / n <= 1e-2
+        scale = 1.0 / max(ref["n_valid"], 1) if red == "mean" else 1.0
+        bound = 2.0 ** -8 * gs.abs() + 1e-7 * scale
+        assert bool(((g - gs).abs() <= bound).all()), float(((g - gs).abs() - bound).max())
+
+
+def _run(logits, target, red, z, in_place=False, want_grad=True):
+    x = logits.to(DEV)
+    loss, grad, n, bad = F.ce_fwd_bwd(x, target.to(DEV), -100, red, z, want_grad=want_grad,
+                                      in_place=in_place)
+    torch.cuda.synchronize()
+    return loss, grad, n, bad, x
+
+
+@pytest.mark.parametrize("z", (0.0, 1e-4))
+@pytest.mark.parametrize("red", ("mean", "sum"))
+def test_small_fp32_workload(z, red):
+    w = workloads.CE_B8_V1000_F32
+    logits, target = workloads.ce_inputs(w)
+    loss, grad, n, bad, _ = _run(logits, target, red, z)
+    _check(logits, target, red, z, loss, grad, n)
+    assert int(bad) == 0
+    loss2, grad2, n2, _, x = _run(logits, target, red, z, in_place=True)
+    assert torch.equal(grad2, grad) and float(loss2) == float(loss)
+
+
+SHAPES = [
+    (3, 1, torch.float32), (5, 7, torch.bfloat16), (5, 9, torch.float32),
+    (7, 2041, torch.bfloat16), (7, 2048, torch.bfloat16), (9, 2049, torch.bfloat16),
+    (64, 4097, torch.bfloat16), (130, 1000, torch.float32), (33, 50257, torch.bfloat16),
+    (17, 50257, torch.float32), (11, 65536, torch.float32), (4, 131073, torch.bfloat16),
+    (6, 70001, torch.float32), (5, 128256, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("B,V,dtype", SHAPES)
+def test_shapes_against_oracle(B, V, dtype):
+    logits, target = workloads.small_ce(B, V, dtype=dtype, sigma=3.0,
+                                        n_ignored=min(2, B - 1), seed=B * 7 + V, boost=8.0)
+    for red, z in (("mean", 1e-4), ("sum", 0.0)):
+        ref = oracle.cross_entropy(logits, target, -100, red, z)
+        loss, grad, n, bad, _ = _run(logits, target, red, z)
+        _check(logits, target, red, z, loss, grad, n, ref=ref)
+        assert int(bad) == 0
+        loss2, grad2, _, _, _ = _run(logits, target, red, z, in_place=True)
+        assert torch.equal(grad2, grad), "in place differs from out of place"
+        assert float(loss2) == float(loss)
+        loss3, g3, _, _, _ = _run(logits, target, red, z, want_grad=False)
+        assert g3 is None and float(loss3) == float(loss)
+
+
+def test_misaligned_rows_and_base():
+    # bf16 rows of odd width, starting 2 bytes past a 16-byte boundary
+    B, V = 12, 50257
+    logits, target = workloads.small_ce(B + 1, V, dtype=torch.bfloat16, sigma=3.0, n_ignored=2,
+                                        seed=3)
+    full = logits.to(DEV)
+    view = full.view(-1)[1:1 + B * V].view(B, V)           # base offset of one element
+    t = target[:B].to(DEV)
+    ref_logits = full.view(-1)[1:1 + B * V].view(B, V).cpu()
+    grad = torch.empty((B * V + 8,), dtype=torch.bfloat16, device=DEV)[1:1 + B * V].view(B, V)
+    loss, g, n, bad = F.ce_fwd_bwd(view, t, -100, "mean", 1e-4, grad=grad)
+    _check(ref_logits, target[:B], "mean", 1e-4, loss, g, n)
+    before = full.clone()
+    loss2, g2, _, _ = F.ce_fwd_bwd(view, t, -100, "mean", 1e-4, in_place=True)
+    assert torch.equal(view, g)
+    # the element before the view was not touched
+    assert torch.equal(full.view(-1)[:1], before.view(-1)[:1])
+
+
+def test_edge_cases():
+    V = 300
+    logits, _ = workloads.small_ce(4, V, dtype=torch.float32, seed=11)
+    allign = torch.full((4,), -100)
+    loss, grad, n, bad, _ = _run(logits, allign, "mean", 0.0)
+    assert math.isnan(float(loss)) and int(n) == 0 and bool((grad == 0).all())
+    loss, grad, n, bad, _ = _run(logits, allign, "sum", 0.0)
+    assert float(loss) == 0.0 and bool((grad == 0).all())
+    # ignore_index inside [0, V) takes precedence over being a class
+    t = torch.tensor([5, 7, 5, 2])
+    x = logits.to(DEV)
+    loss, grad, n, bad = F.ce_fwd_bwd(x, t.to(DEV), 5, "mean", 0.0)
+    ref = oracle.cross_entropy(logits, t, 5, "mean", 0.0)
+    assert int(n) == ref["n_valid"] == 2
+    assert float(loss) == pytest.approx(ref["loss"], rel=1e-5)
+    assert float((grad.double().cpu() - ref["grad"]).abs().max()) <= 1e-6
+    # out-of-range valid targets: flagged, treated as ignored
+    t = torch.tensor([1, V, -3, 2])
+    loss, grad, n, bad = F.ce_fwd_bwd(x, t.to(DEV), -100, "sum", 0.0)
+    assert int(bad) == 1 and int(n) == 2
+    assert bool((grad[1] == 0).all()) and bool((grad[2] == 0).all())
+    tt = torch.tensor([1, -100, -100, 2])
+    ref = oracle.cross_entropy(logits, tt, -100, "sum", 0.0)
+    assert float(loss) == pytest.approx(ref["loss"], rel=1e-5)
+
+
+def test_empty_batch():
+    x = torch.empty((0, 17), dtype=torch.bfloat16, device=DEV)
+    t = torch.empty((0,), dtype=torch.int64, device=DEV)
+    loss, grad, n, bad = F.ce_fwd_bwd(x, t, -100, "mean", 0.0)
+    assert math.isnan(float(loss)) and int(n) == 0 and int(bad) == 0
+    loss, grad, n, bad = F.ce_fwd_bwd(x, t, -100, "sum", 0.0)
+    assert float(loss) == 0.0
+
+
+def test_extreme_logits():
+    # large offsets, -inf entries, and one dominant logit (closed form)
+    V = 5000
+    x = torch.zeros(4, V)
+    x[0] += 3.0e4                      # shift: lse - x_t is log V
+    x[1, 10] = 12.0                    # one dominant logit
+    x[2, ::2] = -float("inf")          # half the row impossible
+    x[3] = torch.linspace(-80, 80, V)
+    t = torch.tensor([3, 10, 1, 4999])
+    for dtype in (torch.float32, torch.bfloat16):
+        xl = x.to(dtype)
+        loss, grad, n, bad, _ = _run(xl, t, "sum", 0.0)
+        ref = oracle.cross_entropy(xl, t, -100, "sum", 0.0)
+        assert math.isfinite(float(loss))
+        tol = 1e-5 if dtype == torch.float32 else 2e-3
+        assert float(loss) == pytest.approx(ref["loss"], rel=tol)
+        assert bool(torch.isfinite(grad).all())
+        assert bool((grad[2, ::2] == 0).all())
+
+
+def test_autograd_wrappers():
+    from lm_head_cross_pass_amd import cross_entropy, cross_entropy_
+    logits, target = workloads.small_ce(16, 3001, dtype=torch.float32, n_ignored=3, seed=5)
+    x = logits.to(DEV).requires_grad_(True)
+    loss = cross_entropy(x, target.to(DEV), -100, "mean", 1e-4)
+    (2.5 * loss).backward()
+    ref = oracle.cross_entropy(logits, target, -100, "mean", 1e-4)
+    assert float(loss.detach()) == pytest.approx(ref["loss"], rel=1e-5)
+    assert float((x.grad.double().cpu() - 2.5 * ref["grad"]).abs().max()) <= 3e-6
+    assert torch.equal(x.detach().cpu(), logits)          # not mutated
+    y = logits.to(DEV)
+    l2 = cross_entropy_(y, target.to(DEV), -100, "mean", 1e-4)
+    assert float(l2) == float(loss.detach())
+    assert float((y.double().cpu() - ref["grad"]).abs().max()) <= 1e-6
+
+
+def test_repeatable_bitwise():
+    logits, target = workloads.small_ce(257, 32001, dtype=torch.bfloat16, n_ignored=9, seed=8)
+    a = _run(logits, target, "mean", 1e-4)
+    b = _run(logits, target, "mean", 1e-4)
+    assert float(a[0]) == float(b[0]) and torch.equal(a[1], b[1])
+
+
+def test_workload_b4096_v50257_bf16_full():
+    w = workloads.CE_B4096_V50257_BF16
+    logits, target = workloads.ce_inputs(w)
+    z, red = w.z_loss[0], w.reductions[0]
+    loss, grad, n, bad, _ = _run(logits, target, red, z)
+    assert int(n) == w.B - w.n_ignored == 3891
+    _check(logits, target, red, z, loss, grad, n)
+
+
+@pytest.mark.slow
+def test_workload_b16384_v128256_bf16_inplace_sampled():
+    w = workloads.CE_B16384_V128256_BF16
+    logits, target = workloads.ce_inputs(w)
+    z, red = w.z_loss[0], w.reductions[0]
+    g = torch.Generator().manual_seed(1)
+    rows = torch.randperm(w.B, generator=g)[:48]
+    ign = (target == -100).nonzero().flatten()[:8]
+    rows = torch.cat([rows, ign, torch.tensor([0, w.B - 1])])
+    x = logits.to(DEV)
+    loss, grad, n, bad = F.ce_fwd_bwd(x, target.to(DEV), -100, red, z, in_place=True)
+    torch.cuda.synchronize()
+    assert int(n) == 16056 and int(bad) == 0
+    # loss over every row, gradient on the sampled rows
+    ref = oracle.cross_entropy(logits, target, -100, red, z, want_grad=False)
+    n_valid, valid = oracle.count_valid(target, -100, w.V)
+    _, _, gref = oracle.cross_entropy_rows(logits[rows], target[rows], valid[rows], 1.0, z)
+    ref["grad"] = gref
+    _check(logits, target, red, z, loss, grad, n, rows=rows, ref=ref)
+    # property at full size: every valid gradient row sums to 0 when z = 0
+    rs = grad.float().sum(dim=1).cpu()
+    assert float(rs.abs().max()) <= 5e-3
