@@ -463,10 +463,24 @@ static int occupancy_grid(const void* fn, int threads, int64_t rows) {
   return static_cast<int>(rows < resident ? rows : resident);
 }
 
+int count_enqueue(const int64_t* target, int64_t B, int64_t V, int64_t ignore_index,
+                  int64_t* n_ws, int64_t* n_user, int32_t* bad_user, hipStream_t stream) {
+  hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, target, B, V, ignore_index,
+                     n_ws, n_user, bad_user);
+  return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
+}
+
+int finish_enqueue(const float* row_loss, int64_t B, const int64_t* n_ws, int reduction,
+                   float* loss, hipStream_t stream) {
+  hipLaunchKernelGGL(ce_finish_kernel, dim3(1), dim3(1024), 0, stream, row_loss, B, n_ws,
+                     reduction, loss);
+  return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
+}
+
 int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
-  hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, stream, p.target, p.B, p.V,
-                     p.ignore_index, p.n_valid_ws, p.n_valid_user, p.bad_user);
-  if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
+  int st = count_enqueue(p.target, p.B, p.V, p.ignore_index, p.n_valid_ws, p.n_valid_user,
+                         p.bad_user, stream);
+  if (st != LMX_OK) return st;
   if (p.B > 0) {
     const int eb = dtype == LMX_BF16 ? 2 : 4;
     const int64_t need = ce_max_row_chunks(reinterpret_cast<uintptr_t>(p.logits), p.V, eb);
@@ -483,10 +497,7 @@ int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
     if (hipLaunchKernel(pick->fn, dim3(grid), dim3(pick->threads), args, 0, stream) != hipSuccess)
       return LMX_ERR_HIP;
   }
-  hipLaunchKernelGGL(ce_finish_kernel, dim3(1), dim3(1024), 0, stream, p.row_loss, p.B,
-                     p.n_valid_ws, p.reduction, p.loss);
-  if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
-  return LMX_OK;
+  return finish_enqueue(p.row_loss, p.B, p.n_valid_ws, p.reduction, p.loss, stream);
 }
 
 }  // namespace lmx

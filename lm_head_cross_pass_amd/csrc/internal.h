@@ -21,6 +21,13 @@ struct CeParams {
   int32_t* bad_user;        // optional output
 };
 
+// N and the out-of-range flag over `target` (one workgroup, no zeroed memory needed).
+int count_enqueue(const int64_t* target, int64_t B, int64_t V, int64_t ignore_index,
+                  int64_t* n_ws, int64_t* n_user, int32_t* bad_user, hipStream_t stream);
+// Fixed-order sum of B row losses, divided by N for mean, into *loss.
+int finish_enqueue(const float* row_loss, int64_t B, const int64_t* n_ws, int reduction,
+                   float* loss, hipStream_t stream);
+
 // Enqueues count -> rows -> finish for one cross-entropy call.
 int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream);
 

@@ -1,0 +1,166 @@
+"""GPU parity of linear_ce against the fp64 oracle (needs an MI355X).
+
+Tolerances (bf16 inputs): loss within 2e-3 relative; grad_inputs and
+grad_weight within 1e-2 relative Frobenius norm of the oracle's exact values;
+N exact. 'weight' accumulation is compared with the oracle's chunk-by-chunk
+bf16 emulation at the same tolerance. The GPU path rounds the logits and the
+logits gradient to bf16 between its matmuls (the matmuls run in bf16); the
+oracle models no intermediate rounding, and the tolerance covers it.
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import linear_ce as olce
+from lm_head_cross_pass_amd import functional as F
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _rel(a, b):
+    b = b.double()
+    n = float(b.norm())
+    d = float((a.double().cpu() - b).norm())
+    return d / n if n > 0 else d
+
+
+def _run(X, W, t, red, z, chunk, accum="fp32"):
+    out = F.linear_ce(X.to(DEV), W.to(DEV), t.to(DEV), -100, red, z, chunk, accum)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    # BT, D, V, chunk
+    (96, 64, 1000, 32),
+    (100, 72, 333, 37),        # ragged last chunk, V not a tile multiple
+    (64, 136, 129, 64),        # one chunk; D not a multiple of 64
+    (257, 128, 4099, 100),
+    (300, 256, 8192, 0),       # default chunk size
+    (1024, 64, 257, 1024),     # one chunk of 1024 rows; ksplit > 1 path
+]
+
+
+@pytest.mark.parametrize("BT,D,V,chunk", CASES)
+def test_shapes_against_oracle(BT, D, V, chunk):
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=max(1, BT // 20), seed=BT + V)
+    for red, z in (("mean", 1e-4), ("sum", 0.0), ("mean", 0.5)):
+        ref = oracle.linear_cross_entropy(X, W, t, -100, red, z)
+        loss, gx, gw, n, bad = _run(X, W, t, red, z, chunk)
+        assert int(n) == ref["n_valid"] and int(bad) == 0
+        assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+        assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+        assert _rel(gw, ref["grad_weight"]) <= 1e-2
+        # ignored rows get exactly zero grad_inputs
+        ign = (t == -100).nonzero().flatten()
+        assert bool((gx[ign.to(DEV)] == 0).all())
+
+
+def test_chunk_size_does_not_change_fp32_results():
+    X, W, t = workloads.small_linear_ce(192, 64, 700, n_ignored=9, seed=4)
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4)
+    outs = [_run(X, W, t, "mean", 1e-4, c) for c in (1, 7, 64, 192)]
+    for loss, gx, gw, n, _ in outs:
+        assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+        assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+        assert _rel(gw, ref["grad_weight"]) <= 1e-2
+    # grad_inputs rows do not depend on the chunking beyond the rounding of G
+    for o in outs[1:]:
+        assert _rel(o[1], outs[0][1].cpu()) <= 1e-2
+
+
+def test_weight_accumulation_follows_the_chunked_rounding():
+    X, W, t = workloads.small_linear_ce(512, 64, 300, n_ignored=10, seed=6)
+    chunk = 16
+    emu = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0, "weight", chunk_size=chunk)
+    exact = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0)
+    loss, gx, gw, n, _ = _run(X, W, t, "sum", 0.0, chunk, "weight")
+    assert float(loss) == pytest.approx(exact["loss"], rel=2e-3)
+    assert _rel(gw, emu["grad_weight"]) <= 1e-2
+    assert _rel(gx, exact["grad_inputs"]) <= 1e-2
+    _, _, gw32, _, _ = _run(X, W, t, "sum", 0.0, chunk, "fp32")
+    assert _rel(gw32, exact["grad_weight"]) <= 1e-2
+    # rounding after each of 32 chunks moves the result toward the emulation
+    d_emu = float((gw.double().cpu() - emu["grad_weight"]).norm())
+    d_exact = float((gw.double().cpu() - exact["grad_weight"]).norm())
+    assert d_emu < d_exact
+
+
+def test_empty_and_all_ignored():
+    X, W, t = workloads.small_linear_ce(40, 64, 100, seed=2)
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    loss, gx, gw, n, _ = F.linear_ce(Xd[:0], Wd, t[:0].to(DEV), -100, "mean", 0.0, 16)
+    assert math.isnan(float(loss)) and int(n) == 0 and bool((gw == 0).all())
+    tt = torch.full((40,), -100)
+    loss, gx, gw, n, _ = F.linear_ce(Xd, Wd, tt.to(DEV), -100, "mean", 0.0, 16)
+    assert math.isnan(float(loss)) and bool((gx == 0).all()) and bool((gw == 0).all())
+    loss, gx, gw, n, _ = F.linear_ce(Xd, Wd, tt.to(DEV), -100, "sum", 0.0, 16)
+    assert float(loss) == 0.0
+
+
+def test_out_of_range_targets_are_flagged():
+    X, W, t = workloads.small_linear_ce(64, 64, 100, seed=3)
+    t = t.clone()
+    t[5] = 100
+    t[9] = -7
+    loss, gx, gw, n, bad = _run(X, W, t, "sum", 0.0, 32)
+    assert int(bad) == 1 and int(n) == 62
+    assert bool((gx[5] == 0).all()) and bool((gx[9] == 0).all())
+    t2 = t.clone()
+    t2[5] = -100
+    t2[9] = -100
+    ref = oracle.linear_cross_entropy(X, W, t2, -100, "sum", 0.0)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+
+
+def test_autograd_wrapper():
+    from lm_head_cross_pass_amd import linear_cross_entropy
+    X, W, t = workloads.small_linear_ce(64, 64, 500, n_ignored=3, seed=7)
+    Xd = X.to(DEV).requires_grad_(True)
+    Wd = W.to(DEV).requires_grad_(True)
+    loss = linear_cross_entropy(Xd, Wd, t.to(DEV), -100, "mean", 1e-4, chunk_size=16)
+    (3.0 * loss).backward()
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4)
+    assert float(loss.detach()) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(Xd.grad, 3.0 * ref["grad_inputs"]) <= 1e-2
+    assert _rel(Wd.grad, 3.0 * ref["grad_weight"]) <= 1e-2
+
+
+def test_repeatable_bitwise():
+    X, W, t = workloads.small_linear_ce(256, 128, 3000, n_ignored=5, seed=9)
+    a = _run(X, W, t, "mean", 1e-4, 64)
+    b = _run(X, W, t, "mean", 1e-4, 64)
+    assert float(a[0]) == float(b[0])
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_workload_bt8192_d768_v50257_full():
+    w = workloads.LCE_BT8192_D768_V50257
+    X, W, t = workloads.linear_ce_inputs(w)
+    loss, gx, gw, n, bad = _run(X, W, t, w.reduction, w.z_loss, w.chunk_size, "fp32")
+    assert int(n) == w.BT - w.n_ignored == 7782
+    ref = oracle.linear_cross_entropy(X, W, t, -100, w.reduction, w.z_loss, block_rows=1024)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("accum", ("fp32", "weight"))
+def test_workload_bt16384_d4096_v128256_sampled(accum):
+    w = workloads.LCE_BT16384_D4096_V128256
+    X, W, t = workloads.linear_ce_inputs(w)
+    loss, gx, gw, n, bad = _run(X, W, t, w.reduction, w.z_loss, w.chunk_size, accum)
+    assert int(n) == 16056 and int(bad) == 0
+    g = torch.Generator().manual_seed(2)
+    rows = torch.randperm(w.BT, generator=g)[:24].tolist()
+    vrows = torch.randperm(w.V, generator=g)[:24].tolist() + [int(t[rows[0]])]
+    ref = olce.linear_cross_entropy_sampled(X, W, t, rows, vrows, -100, w.reduction, w.z_loss,
+                                            block_rows=1024)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx.cpu()[rows], ref["grad_inputs_rows"]) <= 1e-2
+    assert _rel(gw.cpu()[vrows], ref["grad_weight_rows"]) <= 1e-2
