@@ -1,0 +1,263 @@
+"""Throughput of the cross-entropy hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input, inputs already resident in HBM:
+
+* CE fwd+bwd over logits [16384, 128256] bf16 ~ N(0, 3), 2% ignored rows,
+  z = 0, sum reduction, gradient written in place over the logits (each timed
+  step gets its own pre-generated copy of the logits, so every step reads
+  fresh logits);
+* chunked linear-CE with inputs [16384, 4096] bf16 ~ N(0, 1), weight
+  [128256, 4096] bf16 ~ N(0, 0.02), 2% ignored, chunk 2048, mean, z = 0,
+  fp32 grad_weight accumulation.
+
+The JSON line reports the CE leg as ``value`` (GB/s of algorithmic traffic:
+one read of the logits, one write of the gradient, the int64 targets) with its
+roofline against the 8 TB/s HBM peak, and the linear-CE leg under
+``linear_ce`` (TFLOP/s of the three matmuls, 6 BT V D, against the 2.5 PFLOP/s
+dense bf16 MFMA peak), plus its 'weight'-accumulation variant timed on its own.
+``cpu_baseline`` is the fp64 oracle timed on the host on a bounded sample of
+the same CE workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "lm_head_cross_pass_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(counter_file: str, digest: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the source."""
+    path = os.path.join(PROFILES, counter_file)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for ln in open(path):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != digest or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="ce,linear")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--weight-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+    legs = set(args.legs.split(","))
+
+    import torch
+    import workloads
+    from lm_head_cross_pass_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    K, W = args.steps, args.warmup
+
+    # ------------------------------------------------------------ inputs
+    ce_w = workloads.CE_B16384_V128256_BF16
+    lin_w = workloads.LCE_BT16384_D4096_V128256
+    if "ce" in legs:
+        log(f"generating {ce_w.name}")
+        logits_h, target_h = workloads.ce_inputs(ce_w)
+        target = target_h.to(dev)
+        first = logits_h.to(dev)
+        ncopies = K + 1
+        log(f"placing {ncopies} copies of the logits in HBM "
+            f"({ncopies * first.numel() * 2 / 2**30:.1f} GiB)")
+        copies = [first] + [first.clone() for _ in range(ncopies - 1)]
+        ce_ws = torch.empty(_lib.ce_workspace_bytes(ce_w.B, ce_w.V, _lib.LMX_BF16),
+                            dtype=torch.uint8, device=dev)
+        ce_out = [torch.empty((), dtype=torch.float32, device=dev),
+                  torch.empty((), dtype=torch.int64, device=dev),
+                  torch.empty((), dtype=torch.int32, device=dev)]
+
+        def ce_call(x):
+            st = _lib.ce_fwd_bwd(x.data_ptr(), x.data_ptr(), target.data_ptr(), ce_w.B, ce_w.V,
+                                 _lib.LMX_BF16, -100, _lib.LMX_SUM, ce_w.z_loss[0],
+                                 ce_out[0].data_ptr(), ce_out[1].data_ptr(), ce_out[2].data_ptr(),
+                                 ce_ws.data_ptr(), ce_ws.numel(), stream.cuda_stream)
+            _lib.check("ce_fwd_bwd", st)
+    if "linear" in legs:
+        log(f"generating {lin_w.name}")
+        X_h, W_h, t_h = workloads.linear_ce_inputs(lin_w)
+        X, Wt, tl = X_h.to(dev), W_h.to(dev), t_h.to(dev)
+        del X_h, W_h
+        gx, gw = torch.empty_like(X), torch.empty_like(Wt)
+        lin_out = [torch.empty((), dtype=torch.float32, device=dev),
+                   torch.empty((), dtype=torch.int64, device=dev),
+                   torch.empty((), dtype=torch.int32, device=dev)]
+        ws_bytes = max(_lib.linear_ce_workspace_bytes(lin_w.BT, lin_w.D, lin_w.V, _lib.LMX_BF16,
+                                                      lin_w.chunk_size, acc)
+                       for acc in (_lib.LMX_ACC_F32, _lib.LMX_ACC_WEIGHT))
+        lin_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def lin_call(accum):
+            st = _lib.linear_ce(X.data_ptr(), Wt.data_ptr(), tl.data_ptr(), lin_w.BT, lin_w.D,
+                                lin_w.V, _lib.LMX_BF16, -100, _lib.LMX_MEAN, lin_w.z_loss,
+                                lin_w.chunk_size, accum, lin_out[0].data_ptr(), gx.data_ptr(),
+                                gw.data_ptr(), lin_out[1].data_ptr(), lin_out[2].data_ptr(),
+                                lin_ws.data_ptr(), lin_ws.numel(), stream.cuda_stream)
+            _lib.check("linear_ce", st)
+
+    # ------------------------------------------------------------ warmup
+    # copies[0] stays pristine; warmup works in place on copies[1], which is then
+    # restored, and timed step i consumes copies[i + 1]
+    log(f"warmup {W} steps")
+    for i in range(W):
+        if "ce" in legs:
+            ce_call(copies[1])
+        if "linear" in legs:
+            lin_call(_lib.LMX_ACC_F32)
+    if "ce" in legs:
+        copies[1].copy_(copies[0])
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ timed steps
+    log(f"timing {K} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        if "ce" in legs:
+            ce_call(copies[i + 1])
+        ev[i][1].record(stream)
+        if "linear" in legs:
+            lin_call(_lib.LMX_ACC_F32)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / K
+    ce_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    lin_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    log(f"step {wall_ms:.3f} ms (ce {ce_ms:.3f} ms, linear {lin_ms:.3f} ms)")
+
+    line = {
+        "metric": "CE fwd+bwd GB/s (% HBM peak) @V=128256; linear-CE TFLOP/s (% MFMA peak)",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded, shapes and distributions of the workloads)",
+        "config": {"workload": "", "parallelism": "none (one GPU)"},
+    }
+    workload_names = []
+    if "ce" in legs:
+        ce_bytes = 2 * ce_w.B * ce_w.V * 2 + 8 * ce_w.B
+        gbps = ce_bytes / (ce_ms * 1e-3) / 1e9
+        digest = source_digest("ce.hip", "common.h")
+        traffic = stored_traffic("ce_rows_b16384_v128256_bf16.counters.txt", digest)
+        line["value"] = round(gbps, 1)
+        line["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                            "traffic": traffic,
+                            "algorithmic_bytes_per_launch": ce_bytes,
+                            "ms_per_launch": round(ce_ms, 4),
+                            "kernel": "ce_rows_reg_kernel<bf16,1024,16> (+ count, finish)"}
+        workload_names.append(ce_w.name)
+        line["config"].update({"ce_B": ce_w.B, "ce_V": ce_w.V, "ce_reduction": "sum",
+                               "ce_in_place": True})
+    if "linear" in legs:
+        flops = 6.0 * lin_w.BT * lin_w.V * lin_w.D
+        tf = flops / (lin_ms * 1e-3) / 1e12
+        lin = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(lin_ms, 3),
+               "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "algorithmic_flops_per_call": flops,
+                            "kernel": "whole linear_ce call (gemm_nt_kernel x3 per chunk + CE)"}}
+        # 'weight' accumulation, timed on its own
+        if args.weight_steps > 0:
+            lin_call(_lib.LMX_ACC_WEIGHT)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.weight_steps):
+                lin_call(_lib.LMX_ACC_WEIGHT)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wms = e0.elapsed_time(e1) / args.weight_steps
+            lin["weight_accum"] = {"value": round(flops / (wms * 1e-3) / 1e12, 1),
+                                   "unit": "TFLOP/s", "ms_per_call": round(wms, 3)}
+        line["linear_ce"] = lin
+        workload_names.append(lin_w.name)
+        line["config"].update({"lin_BT": lin_w.BT, "lin_D": lin_w.D, "lin_V": lin_w.V,
+                               "lin_chunk": lin_w.chunk_size, "lin_accum": "fp32"})
+        if line["value"] is None:
+            line["value"], line["unit"] = lin["value"], "TFLOP/s"
+    line["config"]["workload"] = " + ".join(workload_names)
+
+    # ------------------------------------------------------------ copy ceiling (context)
+    if "ce" in legs:
+        nb = ce_w.B * ce_w.V * 2
+        src, dst = copies[0], copies[1]
+        _lib.lmx_copy(src.data_ptr(), dst.data_ptr(), nb, stream.cuda_stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            _lib.lmx_copy(src.data_ptr(), dst.data_ptr(), nb, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / 3
+        line["copy_ceiling"] = {"value": round(2 * nb / (cms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                "bytes_moved": 2 * nb}
+
+    # ------------------------------------------------------------ oracle on the host
+    if not args.no_cpu and "ce" in legs:
+        import oracle
+        del copies
+        rows = 2048
+        torch.manual_seed(0)
+        sel = torch.arange(rows)
+        log(f"cpu_baseline: fp64 oracle on {rows} rows of {ce_w.name}")
+        t0 = time.perf_counter()
+        oracle.cross_entropy(logits_h[sel], target_h[sel], -100, "sum", 0.0)
+        dt = time.perf_counter() - t0
+        sb = 2 * rows * ce_w.V * 2 + 8 * rows
+        line["cpu_baseline"] = {"value": round(sb / dt / 1e9, 3), "unit": "GB/s",
+                                "cores": torch.get_num_threads(), "kind": "oracle",
+                                "sample": f"first {rows} of {ce_w.B} rows of the CE workload "
+                                          f"(loss and gradient, fp64), {dt:.1f} s"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
