@@ -90,6 +90,7 @@ int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int
   p.target = target;
   p.B = B;
   p.V = V;
+  p.ld = V;
   p.ignore_index = ignore_index;
   p.z = z_loss_multiplier;
   p.reduction = reduction;

@@ -106,10 +106,10 @@ struct RowView {
 
 template <typename T>
 __device__ __forceinline__ RowView row_view(uintptr_t base, uintptr_t gbase, int64_t row,
-                                            int64_t V) {
+                                            int64_t V, int64_t ld) {
   constexpr int EPC = Elem<T>::kPerChunk;
   RowView r;
-  const uintptr_t a0 = base + static_cast<uintptr_t>(row) * static_cast<uintptr_t>(V) * sizeof(T);
+  const uintptr_t a0 = base + static_cast<uintptr_t>(row) * static_cast<uintptr_t>(ld) * sizeof(T);
   r.first = a0 & ~static_cast<uintptr_t>(15);
   r.lead = static_cast<int>((a0 - r.first) / sizeof(T));
   r.nch = static_cast<int>((r.lead + V + EPC - 1) / EPC);
@@ -172,7 +172,7 @@ template <typename T, int THREADS>
 __device__ __forceinline__ void zero_row(const CeParams& p, int64_t row) {
   constexpr int EPC = Elem<T>::kPerChunk;
   const uintptr_t gb = reinterpret_cast<uintptr_t>(p.grad);
-  const RowView r = row_view<T>(gb, gb, row, p.V);
+  const RowView r = row_view<T>(gb, gb, row, p.V, p.ld);
   float z[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) z[e] = 0.f;
@@ -249,9 +249,9 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
       if (want_grad) zero_row<T, THREADS>(p, row);
       continue;
     }
-    const RowView r = row_view<T>(base, gbase, row, p.V);
+    const RowView r = row_view<T>(base, gbase, row, p.V, p.ld);
     if (tid == 0) {
-      sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.V + t) * sizeof(T));
+      sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.ld + t) * sizeof(T));
     }
     u32x4 d[CPT];
 #pragma unroll
@@ -343,9 +343,9 @@ __global__ __launch_bounds__(THREADS) void ce_rows_stream_kernel(CeParams p) {
       if (want_grad) zero_row<T, THREADS>(p, row);
       continue;
     }
-    const RowView r = row_view<T>(base, gbase, row, p.V);
+    const RowView r = row_view<T>(base, gbase, row, p.V, p.ld);
     if (tid == 0) {
-      sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.V + t) * sizeof(T));
+      sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.ld + t) * sizeof(T));
     }
     float m = -kInf, s = 0.f;
     for (int ci = tid; ci < r.nch; ci += THREADS) {
@@ -442,10 +442,10 @@ const RowKernel* row_kernels(int* count) {
 }  // namespace
 
 // Largest number of 16-byte chunks one row of this call touches.
-int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int elem_bytes) {
+int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int64_t ld, int elem_bytes) {
   const int64_t epc = 16 / elem_bytes;
   const int64_t lead0 = static_cast<int64_t>((base & 15u) / elem_bytes);
-  if ((V * elem_bytes) % 16 == 0) return (lead0 + V + epc - 1) / epc;
+  if ((ld * elem_bytes) % 16 == 0) return (lead0 + V + epc - 1) / epc;
   return (epc - 1 + V + epc - 1) / epc;
 }
 
@@ -477,13 +477,10 @@ int finish_enqueue(const float* row_loss, int64_t B, const int64_t* n_ws, int re
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
-int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
-  int st = count_enqueue(p.target, p.B, p.V, p.ignore_index, p.n_valid_ws, p.n_valid_user,
-                         p.bad_user, stream);
-  if (st != LMX_OK) return st;
+int ce_rows_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
   if (p.B > 0) {
     const int eb = dtype == LMX_BF16 ? 2 : 4;
-    const int64_t need = ce_max_row_chunks(reinterpret_cast<uintptr_t>(p.logits), p.V, eb);
+    const int64_t need = ce_max_row_chunks(reinterpret_cast<uintptr_t>(p.logits), p.V, p.ld, eb);
     int n = 0;
     const RowKernel* ks = dtype == LMX_BF16 ? row_kernels<uint16_t>(&n) : row_kernels<float>(&n);
     const RowKernel* pick = &ks[n - 1];
@@ -497,6 +494,15 @@ int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
     if (hipLaunchKernel(pick->fn, dim3(grid), dim3(pick->threads), args, 0, stream) != hipSuccess)
       return LMX_ERR_HIP;
   }
+  return LMX_OK;
+}
+
+int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
+  int st = count_enqueue(p.target, p.B, p.V, p.ignore_index, p.n_valid_ws, p.n_valid_user,
+                         p.bad_user, stream);
+  if (st != LMX_OK) return st;
+  st = ce_rows_enqueue(p, dtype, stream);
+  if (st != LMX_OK) return st;
   return finish_enqueue(p.row_loss, p.B, p.n_valid_ws, p.reduction, p.loss, stream);
 }
 

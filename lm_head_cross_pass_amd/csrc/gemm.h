@@ -7,21 +7,25 @@
 //
 // Work decomposition:
 // * a workgroup of 256 threads (4 waves as 2 x 2) computes a BM x BN tile,
-//   each wave a (BM/2) x (BN/2) sub-tile as a grid of 32 x 32 MFMA tiles;
-// * K is walked in steps of 64: the next step's A and B tiles are fetched
-//   from global memory into registers (128-bit buffer loads, rows beyond M/N
-//   read as zero by the buffer resource, k beyond K zeroed) while the MFMAs
-//   run on the current step held in LDS, then written to the other half of a
-//   double-buffered LDS stage; one barrier per step;
-// * LDS rows are padded to 72 elements (144 bytes) so the 16-byte fragment
-//   reads of 16 consecutive rows fall in distinct banks;
+//   each wave a (BM/2) x (BN/2) sub-tile as a grid of 32 x 32 MFMA tiles
+//   (128 x 128 per wave at BM = BN = 256: 256 fp32 accumulators per lane);
+// * K is walked in steps of 64. The tiles of the next step are copied from
+//   global memory straight into LDS (buffer_load_dwordx4 ... lds, no staging
+//   registers) while the MFMAs run on the current step: two LDS stages, one
+//   barrier per step;
+// * an LDS tile row is 64 bf16 = 128 bytes = 8 chunks of 16 bytes, stored
+//   without padding with chunk c of row r at slot c ^ f(r),
+//   f(r) = (r ^ (r >> 3)) & 7, so that the 16-byte fragment reads of 8 or 16
+//   consecutive rows hit distinct banks; each wave-wide copy instruction fills
+//   8 rows (1 KiB), each lane fetching the global chunk its slot holds;
+// * rows beyond M / N lie outside the operand's buffer resource and k beyond
+//   K is sent outside it, so both read as zero;
 // * optional split-K: blockIdx enumerates (k-split, tile) pairs and each
 //   split covers a contiguous range of K steps;
 // * workgroup ids are remapped so that each of the 8 XCDs works on a
 //   contiguous range of tiles (tiles that share A or B panels share an L2).
 //
-// The epilogue is a functor called with the accumulators; see Epi* below and
-// in linear_ce.hip.
+// The epilogue is a functor called with the accumulators (see linear_ce.hip).
 #pragma once
 
 #include "common.h"
@@ -30,10 +34,11 @@ namespace lmx {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kGemmThreads = 256;
 constexpr int kGemmBK = 64;
-constexpr int kGemmLdsK = kGemmBK + 8;   // padded LDS row, elements
+constexpr int kRawBufFlags = 0x00020000;
+constexpr int kOutOfRange = static_cast<int>(0x80000000u);   // a buffer offset that reads zero
 
 struct GemmShape {
   const uint16_t* A;
@@ -41,21 +46,33 @@ struct GemmShape {
   const uint16_t* B;
   int64_t ldb;
   int M, N, K;
+  int b_rows;            // rows of B that exist (N may extend past them into zeros)
   int tiles_m, tiles_n;
   int ksplit;            // number of K splits (1 = none)
   int ksteps_per_split;  // K steps of 64 per split
 };
 
+// Block tile BM x BN: 2 x 2 waves for 128 x 128, 2 x 4 waves for 256 x 256;
+// every wave owns a (BM / WAVES_M) x (BN / WAVES_N) sub-tile.
 template <int BM, int BN>
 struct GemmCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WAVES_M = 2;
+  static constexpr int WAVES_N = BN >= 256 ? 4 : 2;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int CPR = kGemmBK / 8;                    // 16-byte chunks per row
-  static constexpr int A_CH = BM * CPR / kGemmThreads;       // chunks per thread
-  static constexpr int B_CH = BN * CPR / kGemmThreads;
-  static constexpr int STAGE = (BM + BN) * kGemmLdsK;       // elements per stage
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int ROWB = kGemmBK * 2;                  // bytes per LDS tile row
+  // LDS: A stage 0, A stage 1, B stage 0, B stage 1
+  static constexpr int A_STAGE = BM * ROWB;
+  static constexpr int B_STAGE = BN * ROWB;
+  static constexpr int B_BASE = 2 * A_STAGE;
+  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
+  static constexpr int A_LOADS = BM / 8 / NWAVES;           // copy instructions per wave
+  static constexpr int B_LOADS = BN / 8 / NWAVES;
 };
+
+__device__ __forceinline__ int lds_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Accumulator coordinates: element r of MFMA tile (i, j) of this lane.
 struct AccCoord {
@@ -67,12 +84,17 @@ struct AccCoord {
   __device__ int col(int j) const { return col0 + j * 32 + (lane & 31); }
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const uint16_t* base, int64_t row0,
-                                                             int rows_left, int rows, int64_t ld) {
+// Buffer resource over up to `rows` rows of a row-major matrix starting at
+// row0; rows past the matrix end are left out, so they read as zero and
+// writes to them are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t row0,
+                                                            int64_t rows_left, int rows,
+                                                            int64_t ld_bytes) {
   const int64_t n = rows_left < rows ? rows_left : rows;
-  const int64_t bytes = n > 0 ? n * ld * 2 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + row0 * ld), 0,
-                                           static_cast<int>(bytes), 0x00020000);
+  const int64_t bytes = n > 0 ? n * ld_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(base) + row0 * ld_bytes), 0,
+      static_cast<int>(bytes), kRawBufFlags);
 }
 
 // Maps blockIdx.x to (split, tile_m, tile_n): tiles of one XCD are contiguous,
@@ -89,14 +111,107 @@ __device__ __forceinline__ void gemm_tile_of_block(const GemmShape& g, int& spli
   tn = t / g.tiles_m;
 }
 
+// s_waitcnt vmcnt(0): this wave's copies into LDS have landed (the barrier
+// that follows makes every wave's copies visible).
+__device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int V> struct IntC { static constexpr int value = V; };
+
+// Threads of the workgroup for a tile size (a plain function, so the launch
+// bounds below read it without template commas).
+template <int AREA>
+constexpr int gemm_threads() { return AREA >= 256 * 256 ? 512 : 256; }
+
+// The pieces of the main loop are device functions rather than lambdas: a
+// lambda is compiled for the host too, where the buffer-resource type and the
+// amdgcn builtins do not exist.
+
+// Copies one K step of A and B into LDS stage `stage`. Lane l of a copy
+// instruction fills LDS slot (l & 7) of row (l >> 3) of an 8-row block, i.e. it
+// fetches global chunk (l & 7) ^ f(row); per lane only the row / chunk part of
+// the offset is kept, the K step's byte offset goes in the scalar offset.
+template <typename C>
+__device__ __forceinline__ void gemm_copy_stage(char* smem, __amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rb, const int* a_voff,
+                                                const int* b_voff, const int* a_kc,
+                                                const int* b_kc, int kbase, int stage, int wave,
+                                                int K) {
+  char* sa = smem + stage * C::A_STAGE + wave * C::A_LOADS * 8 * C::ROWB;
+  char* sb = smem + C::B_BASE + stage * C::B_STAGE + wave * C::B_LOADS * 8 * C::ROWB;
+  if (kbase + kGemmBK <= K) {   // no chunk of this step lies past K
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 8 * C::ROWB), 16,
+                                               a_voff[i], kbase * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 8 * C::ROWB), 16,
+                                               b_voff[i], kbase * 2, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 8 * C::ROWB), 16,
+                                               kbase + a_kc[i] < K ? a_voff[i] : kOutOfRange,
+                                               kbase * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 8 * C::ROWB), 16,
+                                               kbase + b_kc[i] < K ? b_voff[i] : kOutOfRange,
+                                               kbase * 2, 0, 0);
+  }
+}
+
+// Reads the fragments of k slice KK from LDS. A stage is a power-of-two byte
+// size and every offset lies inside stage 0, so switching stage and slice is
+// one XOR with a uniform value.
+template <typename C, int KK>
+__device__ __forceinline__ void gemm_load_frags(const char* smem, const int* a_off,
+                                                const int* b_off, int stage_bytes,
+                                                bf16x8_t* af, bf16x8_t* bfr) {
+  const int flip = stage_bytes | (KK << 5);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(smem + (a_off[i] ^ flip)));
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(smem + (b_off[j] ^ flip)));
+}
+
+template <typename C>
+__device__ __forceinline__ void gemm_mfma_slice(f32x16_t (&acc)[C::FM][C::FN],
+                                                const bf16x8_t* af, const bf16x8_t* bfr) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+// Schedule hint: one LDS read, then a few MFMAs, repeated, so the fragments of
+// slice kk + 1 arrive while the MFMAs of slice kk run.
+template <typename C>
+__device__ __forceinline__ void gemm_interleave_hint() {
+  constexpr int R = C::FM + C::FN, M = C::FM * C::FN;
+  constexpr int PER = (M + R - 1) / R;
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+  }
+}
+
 template <int BM, int BN, typename Epi>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmShape g, Epi epi) {
+__global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(GemmShape g,
+                                                                            Epi epi) {
   using C = GemmCfg<BM, BN>;
-  __shared__ __align__(16) uint16_t smem[C::LDS_BYTES / 2];
+  static_assert(C::THREADS == gemm_threads<BM * BN>(), "thread count");
+  static_assert((C::A_STAGE & (C::A_STAGE - 1)) == 0 && C::A_STAGE == C::B_STAGE,
+                "stage sizes must be equal powers of two");
+  __shared__ __align__(16) char smem[C::LDS_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps LDS bases scalar
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   int split, tm, tn;
   gemm_tile_of_block(g, split, tm, tn);
@@ -106,47 +221,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmShape g, E
   int ke = kb + g.ksteps_per_split;
   if (ke > ksteps) ke = ksteps;
 
-  const __amdgpu_buffer_rsrc_t ra = panel_rsrc(g.A, m0, g.M - m0, BM, g.lda);
-  const __amdgpu_buffer_rsrc_t rb = panel_rsrc(g.B, n0, g.N - n0, BN, g.ldb);
+  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.M - m0, BM, g.lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = rows_rsrc(g.B, n0, g.b_rows - n0, BN, g.ldb * 2);
 
-  u32x4 ra_regs[C::A_CH], rb_regs[C::B_CH];
-  auto fetch = [&](int ks) {
-    const int kbase = ks * kGemmBK;
+  const int lrow = lane >> 3;
+  const int lslot = lane & 7;
+  int a_voff[C::A_LOADS], b_voff[C::B_LOADS], a_kc[C::A_LOADS], b_kc[C::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int q = tid + i * kGemmThreads;
-      const int r = q / C::CPR, kc = q % C::CPR;
-      const int k = kbase + kc * 8;
-      const int off = static_cast<int>((static_cast<int64_t>(r) * g.lda + k) * 2);
-      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-      ra_regs[i] = (k < g.K) ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int r = (wave * C::A_LOADS + i) * 8 + lrow;
+    a_kc[i] = (lslot ^ lds_swz(r)) * 8;
+    a_voff[i] = static_cast<int>((static_cast<int64_t>(r) * g.lda + a_kc[i]) * 2);
+  }
 #pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int q = tid + i * kGemmThreads;
-      const int r = q / C::CPR, kc = q % C::CPR;
-      const int k = kbase + kc * 8;
-      const int off = static_cast<int>((static_cast<int64_t>(r) * g.ldb + k) * 2);
-      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-      rb_regs[i] = (k < g.K) ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto stash = [&](int stage) {
-    uint16_t* sa = smem + stage * C::STAGE;
-    uint16_t* sb = sa + BM * kGemmLdsK;
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int q = tid + i * kGemmThreads;
-      const int r = q / C::CPR, kc = q % C::CPR;
-      *reinterpret_cast<u32x4*>(sa + r * kGemmLdsK + kc * 8) = ra_regs[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int q = tid + i * kGemmThreads;
-      const int r = q / C::CPR, kc = q % C::CPR;
-      *reinterpret_cast<u32x4*>(sb + r * kGemmLdsK + kc * 8) = rb_regs[i];
-    }
-  };
+  for (int i = 0; i < C::B_LOADS; ++i) {
+    const int r = (wave * C::B_LOADS + i) * 8 + lrow;
+    b_kc[i] = (lslot ^ lds_swz(r)) * 8;
+    b_voff[i] = static_cast<int>((static_cast<int64_t>(r) * g.ldb + b_kc[i]) * 2);
+  }
 
   f32x16_t acc[C::FM][C::FN];
 #pragma unroll
@@ -156,45 +248,56 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmShape g, E
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (kb < ke) {
-    fetch(kb);
-    stash(0);
-    __syncthreads();
-  }
+  // Fragment reads: lane l reads 16 bytes of row (l & 31) of each 32-row MFMA
+  // tile, k chunk 2 kk + (l >> 5); the byte offset of slice kk is the slice-0
+  // offset XOR (kk << 5).
   const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
-  for (int ks = kb; ks < ke; ++ks) {
-    const int cur = (ks - kb) & 1;
-    const bool more = ks + 1 < ke;
-    if (more) fetch(ks + 1);
-    const uint16_t* sa = smem + cur * C::STAGE;
-    const uint16_t* sb = sa + BM * kGemmLdsK;
+  const int frag_half = lane >> 5;
+  int a_off[C::FM], b_off[C::FN];
 #pragma unroll
-    for (int kk = 0; kk < kGemmBK / 16; ++kk) {
-      bf16x8_t af[C::FM], bfr[C::FN];
+  for (int i = 0; i < C::FM; ++i) {
+    const int r = wm * C::WM + i * 32 + frag_row;
+    a_off[i] = r * C::ROWB + ((frag_half ^ lds_swz(r)) << 4);
+  }
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int r = wm * C::WM + i * 32 + frag_row;
-        af[i] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4*>(sa + r * kGemmLdsK + kk * 16 + frag_k));
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int r = wn * C::WN + j * 32 + frag_row;
-        bfr[j] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4*>(sb + r * kGemmLdsK + kk * 16 + frag_k));
-      }
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) stash(cur ^ 1);
+  for (int j = 0; j < C::FN; ++j) {
+    const int r = wn * C::WN + j * 32 + frag_row;
+    b_off[j] = C::B_BASE + r * C::ROWB + ((frag_half ^ lds_swz(r)) << 4);
+  }
+  bf16x8_t fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+
+  if (kb < ke) {
+    gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
+                       __builtin_amdgcn_readfirstlane(kb * kGemmBK), 0, wave, g.K);
+    wait_lds_copies();
     __syncthreads();
+    gemm_load_frags<C, 0>(smem, a_off, b_off, 0, fa0, fb0);
+  }
+  for (int ks = kb; ks < ke; ++ks) {
+    const int cur = __builtin_amdgcn_readfirstlane((ks - kb) & 1);
+    const int cur_bytes = cur * C::A_STAGE, nxt_bytes = (cur ^ 1) * C::A_STAGE;
+    const bool more = ks + 1 < ke;
+    if (more) {
+      gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
+                         __builtin_amdgcn_readfirstlane((ks + 1) * kGemmBK), cur ^ 1, wave, g.K);
+    }
+    gemm_load_frags<C, 1>(smem, a_off, b_off, cur_bytes, fa1, fb1);
+    gemm_mfma_slice<C>(acc, fa0, fb0);
+    gemm_interleave_hint<C>();
+    gemm_load_frags<C, 2>(smem, a_off, b_off, cur_bytes, fa0, fb0);
+    gemm_mfma_slice<C>(acc, fa1, fb1);
+    gemm_interleave_hint<C>();
+    gemm_load_frags<C, 3>(smem, a_off, b_off, cur_bytes, fa1, fb1);
+    gemm_mfma_slice<C>(acc, fa0, fb0);
+    gemm_interleave_hint<C>();
+    gemm_mfma_slice<C>(acc, fa1, fb1);
+    wait_lds_copies();
+    __syncthreads();   // next stage landed; this stage is free for the copy after next
+    if (more) gemm_load_frags<C, 0>(smem, a_off, b_off, nxt_bytes, fa0, fb0);
   }
   AccCoord ac{wm * C::WM, wn * C::WN, lane};
-  epi.template run<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, split, g, smem);
+  epi.template run<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, split, g,
+                                         reinterpret_cast<uint16_t*>(smem));
 }
 
 }  // namespace lmx

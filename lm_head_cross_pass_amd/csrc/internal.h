@@ -11,6 +11,7 @@ struct CeParams {
   void* grad;               // [B, V] or nullptr (loss only); may equal logits
   const int64_t* target;    // [B]
   int64_t B, V;
+  int64_t ld;               // row stride of logits and grad, in elements (>= V)
   int64_t ignore_index;
   float z;                  // z_loss_multiplier
   int reduction;            // LMX_MEAN / LMX_SUM
@@ -28,11 +29,15 @@ int count_enqueue(const int64_t* target, int64_t B, int64_t V, int64_t ignore_in
 int finish_enqueue(const float* row_loss, int64_t B, const int64_t* n_ws, int reduction,
                    float* loss, hipStream_t stream);
 
+// Enqueues only the row kernel (loss terms into row_loss, gradient), with N
+// already in *n_valid_ws.
+int ce_rows_enqueue(const CeParams& p, int dtype, hipStream_t stream);
+
 // Enqueues count -> rows -> finish for one cross-entropy call.
 int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream);
 
 // Largest number of 16-byte chunks any row touches (for kernel selection).
-int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int elem_bytes);
+int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int64_t ld, int elem_bytes);
 
 // Workspace layout of ce_fwd_bwd.
 struct CeWorkspace {
@@ -61,10 +66,8 @@ struct LinearCeParams {
 struct LinearCeWorkspace {
   int64_t ldv;              // padded vocabulary stride of the chunk buffers
   int64_t ldc;              // padded chunk-row stride of the transposed buffers
-  int64_t ntn;              // vocabulary tiles of the logits GEMM
   int64_t ksplit;           // K splits of the grad_inputs GEMM
-  size_t n_valid_off, row_loss_off, lse_off, part_off, z_off, gt_off, xt_off, wt_off,
-      dxp_off, dw_off, total;
+  size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, dxp_off, dw_off, total;
 };
 LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, int64_t chunk,
                                              int accum);

@@ -7,22 +7,21 @@
 //             scaled); W^T [D, ldv] (zero-padded) for the grad_inputs GEMM.
 // Per chunk of C rows (r0 .. r0 + C'):
 //   1. X_c^T [D, ldc]                                  transpose
-//   2. Z = X_c W^T (bf16) and per (row, 128-column tile) (max, sum exp)
-//                                                      MFMA GEMM, CE-stats epilogue
-//   3. lse per row, row loss terms                     one wave per row
-//   4. G = scale ((1 + 2 z lse) softmax - onehot) over Z, in place, and G^T
-//                                                      64 x 64 tiles through LDS
+//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM
+//   3. the cross-entropy row kernel on Z, in place: loss terms and
+//      G = scale ((1 + 2 z lse) softmax - onehot)      same kernel as ce_fwd_bwd
+//   4. G^T [ldv, ldc]                                  transpose
 //   5. grad_inputs[r0:] = G W                          MFMA GEMM (split-K if the
 //                                                      tile count cannot fill the chip)
-//   6. dW (+)= G^T X_c                                 MFMA GEMM, read-modify-write epilogue
+//   6. dW (+)= G^T X_c                                 MFMA GEMM, accumulate epilogue
 // Finally the fixed-order loss reduction. In 'fp32' accumulation dW lives in
 // an fp32 workspace and the last chunk's epilogue writes the rounded bf16
 // result; in 'weight' accumulation the bf16 grad_weight itself is updated per
 // chunk (rounded to nearest even after each chunk).
 //
 // The logits and G are kept in bf16 between steps, as bf16 matmuls produce
-// them; the (max, sum exp) statistics are taken from the rounded logits, so G
-// is exactly the cross-entropy gradient of the bf16 logits up to fp32 rounding.
+// them; the cross-entropy of a chunk is computed in fp32 from the rounded
+// logits, so G is the cross-entropy gradient of the bf16 logits.
 #include "gemm.h"
 #include "internal.h"
 
@@ -30,7 +29,8 @@ namespace lmx {
 
 namespace {
 
-constexpr int kTile = 128;        // GEMM tile (BM = BN) of all three products
+constexpr int kTileS = 128;       // small GEMM tile (BM = BN), two workgroups per CU
+constexpr int kTileL = 256;       // large GEMM tile, one workgroup per CU
 constexpr int kLdvAlign = 256;    // vocabulary padding of the chunk buffers
 constexpr int kLdcAlign = 64;     // chunk-row padding of the transposed buffers
 constexpr size_t kWsAlign = 256;
@@ -40,70 +40,9 @@ int64_t round_up64(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // ------------------------------------------------------------------ epilogues
 
-// Step 2: logits tile -> bf16 chunk buffer, plus per-row (max, sum exp) of the
-// tile's valid columns.
-struct EpiLogits {
-  uint16_t* z;
-  int64_t ldz;
-  float2* part;     // [tiles_n][ldp]
-  int64_t ldp;
-  int V;
-
-  template <int BM, int BN, int FM, int FN>
-  __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int,
-                      const GemmShape& g, uint16_t* smem) {
-    constexpr int LD = BN + 8;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          smem[ac.row(i, r) * LD + ac.col(j)] = f32_to_bf16_bits(acc[i][j][r]);
-    __syncthreads();
-    constexpr int TPR = kGemmThreads / BM;   // threads per row
-    constexpr int CPT = BN / TPR;            // columns per thread
-    const int tid = threadIdx.x;
-    const int row = tid / TPR, h = tid % TPR;
-    const int c0 = h * CPT;
-    const bool row_ok = m0 + row < g.M;
-    float m = -kInf;
-    u32x4 v[CPT / 8];
-#pragma unroll
-    for (int q = 0; q < CPT / 8; ++q) {
-      v[q] = *reinterpret_cast<const u32x4*>(smem + row * LD + c0 + q * 8);
-      if (row_ok) {
-        *reinterpret_cast<u32x4*>(z + static_cast<int64_t>(m0 + row) * ldz + n0 + c0 + q * 8) =
-            v[q];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (e & 1) ? bf16_hi(v[q][e >> 1]) : bf16_lo(v[q][e >> 1]);
-        if (n0 + c0 + q * 8 + e < V) m = fmaxf(m, x);
-      }
-    }
-    float s = 0.f;
-    if (m != -kInf) {
-#pragma unroll
-      for (int q = 0; q < CPT / 8; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (e & 1) ? bf16_hi(v[q][e >> 1]) : bf16_lo(v[q][e >> 1]);
-          if (n0 + c0 + q * 8 + e < V) s += exp2_fast((x - m) * kLog2e);
-        }
-    }
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) {
-      const float m2 = __shfl_xor(m, off, 64);
-      const float s2 = __shfl_xor(s, off, 64);
-      lse_combine(m, s, m2, s2);
-    }
-    if (h == 0 && row_ok) part[static_cast<int64_t>(n0 / BN) * ldp + m0 + row] = make_float2(m, s);
-  }
-};
-
-// Step 5: grad_inputs rows (bf16), or fp32 split-K partials.
-struct EpiDx {
+// Steps 2 and 5: a bf16 output tile (logits, grad_inputs rows), or fp32
+// split-K partials.
+struct EpiBf16 {
   uint16_t* out;
   int64_t ldo;
   float* partial;   // [ksplit][M][ldp]
@@ -112,55 +51,89 @@ struct EpiDx {
   template <int BM, int BN, int FM, int FN>
   __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int split,
                       const GemmShape& g, uint16_t*) {
+    const bool direct = g.ksplit == 1;
+    const __amdgpu_buffer_rsrc_t ro =
+        direct ? rows_rsrc(out, m0, g.M - m0, BM, ldo * 2)
+               : rows_rsrc(partial + static_cast<int64_t>(split) * g.M * ldp, m0, g.M - m0, BM,
+                           ldp * 4);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + ac.col(j);
+      if (col >= g.N) continue;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + ac.row(i, r), col = n0 + ac.col(j);
-          if (row < g.M && col < g.N) {
-            if (g.ksplit == 1) {
-              out[static_cast<int64_t>(row) * ldo + col] = f32_to_bf16_bits(acc[i][j][r]);
-            } else {
-              partial[(static_cast<int64_t>(split) * g.M + row) * ldp + col] = acc[i][j][r];
-            }
+          const int row = ac.row(i, r);   // tile-local; rows >= M fall outside the resource
+          if (direct) {
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[i][j][r]), ro,
+                                                  (row * static_cast<int>(ldo) + col) * 2, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro,
+                                                  (row * static_cast<int>(ldp) + col) * 4, 0, 0);
           }
         }
+    }
   }
 };
 
 enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToBf16 = 2, kDwStoreBf16 = 3, kDwAddBf16 = 4 };
 
-// Step 6: grad_weight accumulation.
+// Step 6: grad_weight accumulation. The middle chunks of the fp32 mode add
+// with buffer_atomic_add_f32, which returns nothing: the read-modify-write of
+// the fp32 accumulator happens in L2 while the workgroup moves on. Each
+// element has exactly one writer per launch and the launches are ordered, so
+// the result is the same as a plain read-modify-write, bit for bit.
 struct EpiDw {
   float* acc32;     // [V][ld] fp32 accumulator ('fp32' mode)
   uint16_t* out16;  // [V][ld] bf16 grad_weight
   int64_t ld;
   int mode;
 
+  template <int MODE, int FM, int FN>
+  __device__ void apply(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int n0, const GemmShape& g,
+                        __amdgpu_buffer_rsrc_t r32, __amdgpu_buffer_rsrc_t r16) {
+    const int ldi = static_cast<int>(ld);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + ac.col(j);
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = ac.row(i, r) * ldi + col;   // tile-local row; rows >= M are dropped
+          const float v = acc[i][j][r];
+          if constexpr (MODE == kDwStoreF32) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r32, e * 4, 0, 0);
+          } else if constexpr (MODE == kDwAddF32) {
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r32, e * 4, 0, 0);
+          } else if constexpr (MODE == kDwAddF32ToBf16) {
+            const float o = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r32, e * 4, 0, 0));
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o + v), r16, e * 2, 0, 0);
+          } else if constexpr (MODE == kDwStoreBf16) {
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r16, e * 2, 0, 0);
+          } else {
+            const uint16_t o = __builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(bf16_bits_to_f32(o) + v), r16,
+                                                  e * 2, 0, 0);
+          }
+        }
+    }
+  }
+
   template <int BM, int BN, int FM, int FN>
   __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int,
                       const GemmShape& g, uint16_t*) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + ac.row(i, r), col = n0 + ac.col(j);
-          if (row < g.M && col < g.N) {
-            const int64_t idx = static_cast<int64_t>(row) * ld + col;
-            const float v = acc[i][j][r];
-            switch (mode) {
-              case kDwStoreF32: acc32[idx] = v; break;
-              case kDwAddF32: acc32[idx] += v; break;
-              case kDwAddF32ToBf16: out16[idx] = f32_to_bf16_bits(acc32[idx] + v); break;
-              case kDwStoreBf16: out16[idx] = f32_to_bf16_bits(v); break;
-              default: out16[idx] = f32_to_bf16_bits(bf16_bits_to_f32(out16[idx]) + v); break;
-            }
-          }
-        }
+    const __amdgpu_buffer_rsrc_t r32 = rows_rsrc(acc32, m0, g.M - m0, BM, ld * 4);
+    const __amdgpu_buffer_rsrc_t r16 = rows_rsrc(out16, m0, g.M - m0, BM, ld * 2);
+    switch (mode) {
+      case kDwStoreF32: apply<kDwStoreF32>(acc, ac, n0, g, r32, r16); break;
+      case kDwAddF32: apply<kDwAddF32>(acc, ac, n0, g, r32, r16); break;
+      case kDwAddF32ToBf16: apply<kDwAddF32ToBf16>(acc, ac, n0, g, r32, r16); break;
+      case kDwStoreBf16: apply<kDwStoreBf16>(acc, ac, n0, g, r32, r16); break;
+      default: apply<kDwAddBf16>(acc, ac, n0, g, r32, r16); break;
+    }
   }
 };
 
@@ -208,106 +181,6 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
-// Step 3: lse of each chunk row from the per-tile statistics, and its loss term.
-__global__ __launch_bounds__(256) void chunk_lse_kernel(const float2* __restrict__ part,
-                                                        int tiles_n, int64_t ldp,
-                                                        const uint16_t* __restrict__ z,
-                                                        int64_t ldz,
-                                                        const int64_t* __restrict__ target,
-                                                        int rows, int V, int64_t ignore_index,
-                                                        float zl, float* __restrict__ lse_out,
-                                                        float* __restrict__ row_loss) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float m = -kInf, s = 0.f;
-  for (int tn = lane; tn < tiles_n; tn += 64) {
-    const float2 ps = part[static_cast<int64_t>(tn) * ldp + row];
-    lse_combine(m, s, ps.x, ps.y);
-  }
-  wave_lse_combine(m, s);
-  if (lane == 0) {
-    const int64_t t = target[row];
-    const bool valid = t != ignore_index && t >= 0 && t < V;
-    const float log_s = log2_fast(s) * kLn2;
-    const float lse = m + log_s;
-    lse_out[row] = lse;
-    float l = 0.f;
-    if (valid) {
-      const float zt = bf16_bits_to_f32(z[static_cast<int64_t>(row) * ldz + t]);
-      l = (m - zt) + log_s + zl * lse * lse;
-    }
-    row_loss[row] = l;
-  }
-}
-
-// Step 4: G over the chunk logits (in place) and G^T, 64 x 64 tiles.
-__global__ __launch_bounds__(256) void chunk_grad_kernel(uint16_t* __restrict__ zg, int64_t ldz,
-                                                         uint16_t* __restrict__ gt, int64_t ldt,
-                                                         const float* __restrict__ lse,
-                                                         const int64_t* __restrict__ target,
-                                                         const int64_t* __restrict__ n_ws,
-                                                         int reduction, float zl, int rows,
-                                                         int V, int64_t ignore_index) {
-  __shared__ uint16_t t[64][64 + 2];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  const float scale = reduction == LMX_MEAN ? 1.0f / static_cast<float>(*n_ws) : 1.0f;
-  {
-    const int rr = tid / 4, cc = (tid % 4) * 16;
-    const int r = r0 + rr;
-    bool valid = false;
-    int64_t tg = -1;
-    float lr = 0.f;
-    if (r < rows) {
-      tg = target[r];
-      valid = tg != ignore_index && tg >= 0 && tg < V;
-      lr = lse[r];
-    }
-    const float c = scale * (1.f + 2.f * zl * lr);
-    const float comb = lr * kLog2e;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int col = c0 + cc + q * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < rows) v = *reinterpret_cast<const u32x4*>(zg + static_cast<int64_t>(r) * ldz + col);
-      float gv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-        float gval = 0.f;
-        if (valid && col + e < V) {
-          gval = c * exp2_fast(__builtin_fmaf(x, kLog2e, -comb));
-          if (col + e == tg) gval -= scale;
-        }
-        gv[e] = gval;
-      }
-      u32x4 o = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]),
-                 pack_bf16x2(gv[4], gv[5]), pack_bf16x2(gv[6], gv[7])};
-      if (r < rows) *reinterpret_cast<u32x4*>(zg + static_cast<int64_t>(r) * ldz + col) = o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[rr][cc + q * 8 + 2 * e] = static_cast<uint16_t>(o[e] & 0xffffu);
-        t[rr][cc + q * 8 + 2 * e + 1] = static_cast<uint16_t>(o[e] >> 16);
-      }
-    }
-  }
-  __syncthreads();
-  {
-    const int cc = tid / 4, rr = (tid % 4) * 16;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = static_cast<uint32_t>(t[rr + q * 8 + 2 * e][cc]) |
-               (static_cast<uint32_t>(t[rr + q * 8 + 2 * e + 1][cc]) << 16);
-      }
-      *reinterpret_cast<u32x4*>(gt + static_cast<int64_t>(c0 + cc) * ldt + r0 + rr + q * 8) = v;
-    }
-  }
-}
-
 // grad_inputs rows = bf16(sum over splits of the fp32 partials), fixed order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
                                                             int ksplit, int M, int N,
@@ -337,16 +210,33 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* p, int64_t n) {
 // ------------------------------------------------------------------ host helpers
 
 template <typename Epi>
-int launch_gemm(const GemmShape& g, const Epi& epi, hipStream_t stream) {
+int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream) {
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
-  hipLaunchKernelGGL((gemm_nt_kernel<kTile, kTile, Epi>), dim3(blocks), dim3(kGemmThreads), 0,
-                     stream, g, epi);
+  if (tile == kTileL) {
+    constexpr int threads = GemmCfg<kTileL, kTileL>::THREADS;
+    hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi>), dim3(blocks), dim3(threads), 0,
+                       stream, g, epi);
+  } else {
+    constexpr int threads = GemmCfg<kTileS, kTileS>::THREADS;
+    hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi>), dim3(blocks), dim3(threads), 0,
+                       stream, g, epi);
+  }
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
+// The large tile when it yields at least one workgroup per CU of the chip
+// (256 CUs), else the small one.
+int pick_tile(int64_t M, int64_t N) {
+  const int64_t big = ((M + kTileL - 1) / kTileL) * ((N + kTileL - 1) / kTileL);
+  return big >= 256 ? kTileL : kTileS;
+}
+
+// C[M, N] = A[M, K] B[N, K]^T where only the first b_rows rows of B exist
+// (the rest of N reads as zeros).
 GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N,
-                     int K, int ksplit) {
+                     int b_rows, int K, int ksplit, int tile) {
+  const int kTile = tile;
   GemmShape g;
   g.A = A;
   g.lda = lda;
@@ -354,6 +244,7 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.ldb = ldb;
   g.M = M;
   g.N = N;
+  g.b_rows = b_rows;
   g.K = K;
   g.tiles_m = (M + kTile - 1) / kTile;
   g.tiles_n = (N + kTile - 1) / kTile;
@@ -375,11 +266,13 @@ int transpose_pad(const uint16_t* src, int64_t ld_src, int R, int Cs, uint16_t* 
 }
 
 // K splits of the grad_inputs product: enough (split, tile) pairs to give every
-// CU two workgroups, but at least 4 K steps per split.
+// CU its resident workgroups, but at least 4 K steps per split.
 int dx_ksplit(int64_t C, int64_t D, int64_t ldv) {
-  const int64_t tiles = ((C + kTile - 1) / kTile) * ((D + kTile - 1) / kTile);
+  const int tile = pick_tile(C, D);
+  const int64_t tiles = ((C + tile - 1) / tile) * ((D + tile - 1) / tile);
+  const int64_t slots = tile == kTileL ? 256 : 512;
   const int64_t ksteps = ldv / kGemmBK;
-  int64_t s = (512 + tiles - 1) / tiles;
+  int64_t s = (slots + tiles - 1) / tiles;
   if (s > ksteps / 4) s = ksteps / 4;
   if (s < 1) s = 1;
   return static_cast<int>(s);
@@ -405,7 +298,6 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   const int64_t C = chunk > 0 ? chunk : 1;
   w.ldv = round_up64(V, kLdvAlign);
   w.ldc = round_up64(C, kLdcAlign);
-  w.ntn = w.ldv / kTile;
   w.ksplit = dx_ksplit(C, D, w.ldv);
   const int64_t nchunks = BT > 0 ? (BT + C - 1) / C : 0;
   size_t off = 0;
@@ -416,8 +308,6 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   };
   w.n_valid_off = take(8);
   w.row_loss_off = take(static_cast<size_t>(BT) * 4);
-  w.lse_off = take(static_cast<size_t>(C) * 4);
-  w.part_off = take(static_cast<size_t>(w.ntn) * C * 8);
   w.z_off = take(static_cast<size_t>(C) * w.ldv * 2);
   w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldc * 2);
   w.xt_off = take(static_cast<size_t>(D) * w.ldc * 2);
@@ -433,8 +323,6 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
   char* ws = static_cast<char*>(ws_base);
   int64_t* n_ws = reinterpret_cast<int64_t*>(ws + wl.n_valid_off);
   float* row_loss = reinterpret_cast<float*>(ws + wl.row_loss_off);
-  float* lse = reinterpret_cast<float*>(ws + wl.lse_off);
-  float2* part = reinterpret_cast<float2*>(ws + wl.part_off);
   uint16_t* z = reinterpret_cast<uint16_t*>(ws + wl.z_off);
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
   uint16_t* xt = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
@@ -464,28 +352,41 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
     // 1. X_c^T
     st = transpose_pad(xc, p.D, rows, D, xt, ldc, static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
-    // 2. logits and per-tile statistics
+    // 2. logits Z = X_c W^T over all ldv columns (columns >= V read zero rows of W)
     {
-      GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, V, D, 1);
-      EpiLogits e{z, ldv, part, p.chunk, V};
-      st = launch_gemm(g, e, stream);
+      const int tile = pick_tile(rows, ldv);
+      GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
+      EpiBf16 e{z, ldv, nullptr, 0};
+      st = launch_gemm(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
-    // 3. lse and loss terms
-    hipLaunchKernelGGL(chunk_lse_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, part,
-                       static_cast<int>((V + kTile - 1) / kTile), p.chunk, z, ldv, tc, rows, V,
-                       p.ignore_index, p.z, lse, row_loss + r0);
-    if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
-    // 4. G in place, and G^T
-    hipLaunchKernelGGL(chunk_grad_kernel, dim3(ldv / 64, ldc / 64), dim3(256), 0, stream, z, ldv,
-                       gt, ldc, lse, tc, n_ws, p.reduction, p.z, rows, V, p.ignore_index);
-    if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
+    // 3. cross-entropy of the chunk rows, G written over Z, loss terms
+    {
+      CeParams cp{};
+      cp.logits = z;
+      cp.grad = z;
+      cp.target = tc;
+      cp.B = rows;
+      cp.V = p.V;
+      cp.ld = ldv;
+      cp.ignore_index = p.ignore_index;
+      cp.z = p.z;
+      cp.reduction = p.reduction;
+      cp.n_valid_ws = n_ws;
+      cp.row_loss = row_loss + r0;
+      st = ce_rows_enqueue(cp, LMX_BF16, stream);
+      if (st != LMX_OK) return st;
+    }
+    // 4. G^T for the grad_weight product
+    st = transpose_pad(z, ldv, rows, V, gt, ldc, static_cast<int>(ldc), stream);
+    if (st != LMX_OK) return st;
     // 5. grad_inputs rows
     {
-      GemmShape g = make_shape(z, ldv, wt, ldv, rows, D, static_cast<int>(ldv),
-                               static_cast<int>(wl.ksplit));
-      EpiDx e{p.grad_x + r0 * p.D, p.D, dxp, p.D};
-      st = launch_gemm(g, e, stream);
+      const int tile = pick_tile(p.chunk, D);   // the tile the workspace was sized for
+      GemmShape g = make_shape(z, ldv, wt, ldv, rows, D, D, static_cast<int>(ldv),
+                               static_cast<int>(wl.ksplit), tile);
+      EpiBf16 e{p.grad_x + r0 * p.D, p.D, dxp, p.D};
+      st = launch_gemm(g, tile, e, stream);
       if (st != LMX_OK) return st;
       if (g.ksplit > 1) {
         const int64_t total = static_cast<int64_t>(rows) * D / 4;
@@ -504,9 +405,10 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       } else {
         mode = first ? kDwStoreBf16 : kDwAddBf16;
       }
-      GemmShape g = make_shape(gt, ldc, xt, ldc, V, D, static_cast<int>(ldc), 1);
+      const int tile = pick_tile(V, D);
+      GemmShape g = make_shape(gt, ldc, xt, ldc, V, D, D, static_cast<int>(ldc), 1, tile);
       EpiDw e{dw, p.grad_w, p.D, mode};
-      st = launch_gemm(g, e, stream);
+      st = launch_gemm(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
   }

@@ -36,6 +36,17 @@ def test_every_declared_function_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_library_binds_every_symbol_eagerly():
+    # every kernel's host stub must be defined: a lazily bound library would
+    # only fail at the first launch of a kernel whose stub is missing
+    import subprocess
+    import sys
+    code = ("import ctypes, os, sys; ctypes.CDLL(sys.argv[1], mode=os.RTLD_NOW); print('ok')")
+    r = subprocess.run([sys.executable, "-c", code, _lib.LIB_PATH], capture_output=True,
+                       text=True)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr
+
+
 def test_only_the_abi_is_exported():
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
