@@ -9,15 +9,18 @@
 // * a workgroup of 256 threads (4 waves as 2 x 2) computes a BM x BN tile,
 //   each wave a (BM/2) x (BN/2) sub-tile as a grid of 32 x 32 MFMA tiles
 //   (128 x 128 per wave at BM = BN = 256: 256 fp32 accumulators per lane);
-// * K is walked in steps of 64. The tiles of the next step are copied from
-//   global memory straight into LDS (buffer_load_dwordx4 ... lds, no staging
-//   registers) while the MFMAs run on the current step: two LDS stages, one
-//   barrier per step;
-// * an LDS tile row is 64 bf16 = 128 bytes = 8 chunks of 16 bytes, stored
-//   without padding with chunk c of row r at slot c ^ f(r),
-//   f(r) = (r ^ (r >> 3)) & 7, so that the 16-byte fragment reads of 8 or 16
-//   consecutive rows hit distinct banks; each wave-wide copy instruction fills
-//   8 rows (1 KiB), each lane fetching the global chunk its slot holds;
+// * K is walked in steps of BK = 64 through a ring of LDS stages (two by
+//   default): the tiles of the next step are copied from global memory
+//   straight into LDS (buffer_load_dwordx4 ... lds, no staging registers)
+//   while the MFMAs run on the current one; one barrier per step. (BK = 32
+//   with a deeper ring is supported too; on these shapes it measured slower:
+//   its 64-byte row segments halve the size of each memory request.)
+// * an LDS tile row of BK bf16 is BK / 8 chunks of 16 bytes, stored without
+//   padding with chunk c of row r at slot c ^ f(r) (f(r) = (r ^ (r >> 3)) & 7
+//   for 8 chunks, ((r >> 1) ^ (r >> 3)) & 3 for 4), so that the 16-byte
+//   fragment reads of 8 or 16 consecutive rows hit distinct banks; each
+//   wave-wide copy instruction fills 1 KiB of rows, each lane fetching the
+//   global chunk its slot holds;
 // * rows beyond M / N lie outside the operand's buffer resource and k beyond
 //   K is sent outside it, so both read as zero;
 // * optional split-K: blockIdx enumerates (k-split, tile) pairs and each
@@ -36,7 +39,14 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kGemmBK = 64;
+#ifndef LMX_GEMM_BK
+#define LMX_GEMM_BK 64
+#endif
+#ifndef LMX_GEMM_STAGES
+#define LMX_GEMM_STAGES 2
+#endif
+constexpr int kGemmBK = LMX_GEMM_BK;          // K per step
+constexpr int kGemmStages = LMX_GEMM_STAGES;  // LDS ring depth
 constexpr int kRawBufFlags = 0x00020000;
 constexpr int kOutOfRange = static_cast<int>(0x80000000u);   // a buffer offset that reads zero
 
@@ -49,7 +59,7 @@ struct GemmShape {
   int b_rows;            // rows of B that exist (N may extend past them into zeros)
   int tiles_m, tiles_n;
   int ksplit;            // number of K splits (1 = none)
-  int ksteps_per_split;  // K steps of 64 per split
+  int ksteps_per_split;  // K steps per split
 };
 
 // Block tile BM x BN: 2 x 2 waves for 128 x 128, 2 x 4 waves for 256 x 256;
@@ -63,16 +73,26 @@ struct GemmCfg {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int ROWB = kGemmBK * 2;                  // bytes per LDS tile row
-  // LDS: A stage 0, A stage 1, B stage 0, B stage 1
+  static constexpr int CPR = kGemmBK / 8;                   // 16-byte chunks per row
+  static constexpr int ROWS_PER_COPY = 1024 / ROWB;         // rows one copy instruction fills
+  static_assert(kGemmStages >= 2, "at least two LDS stages");
+  // LDS: A stages 0..3, then B stages 0..3
   static constexpr int A_STAGE = BM * ROWB;
   static constexpr int B_STAGE = BN * ROWB;
-  static constexpr int B_BASE = 2 * A_STAGE;
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
-  static constexpr int A_LOADS = BM / 8 / NWAVES;           // copy instructions per wave
-  static constexpr int B_LOADS = BN / 8 / NWAVES;
+  static constexpr int B_BASE = kGemmStages * A_STAGE;
+  static constexpr int LDS_BYTES = kGemmStages * (A_STAGE + B_STAGE);
+  static constexpr int A_LOADS = BM / ROWS_PER_COPY / NWAVES;   // copy instructions per wave
+  static constexpr int B_LOADS = BN / ROWS_PER_COPY / NWAVES;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
 };
 
-__device__ __forceinline__ int lds_swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Slot swizzle of an LDS row of CPR 16-byte chunks (CPR = 4 or 8): 8 or 16
+// consecutive rows reading the same logical chunk hit distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
 // Accumulator coordinates: element r of MFMA tile (i, j) of this lane.
 struct AccCoord {
@@ -111,9 +131,15 @@ __device__ __forceinline__ void gemm_tile_of_block(const GemmShape& g, int& spli
   tn = t / g.tiles_m;
 }
 
-// s_waitcnt vmcnt(0): this wave's copies into LDS have landed (the barrier
-// that follows makes every wave's copies visible).
-__device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone): at most N of this
+// wave's vector memory operations, i.e. of its copies into LDS, are still in
+// flight. Copies complete in issue order, so this waits for all but the last
+// N. The barrier that follows makes every wave's copies visible.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 template <int V> struct IntC { static constexpr int value = V; };
 
@@ -127,35 +153,35 @@ constexpr int gemm_threads() { return AREA >= 256 * 256 ? 512 : 256; }
 // amdgcn builtins do not exist.
 
 // Copies one K step of A and B into LDS stage `stage`. Lane l of a copy
-// instruction fills LDS slot (l & 7) of row (l >> 3) of an 8-row block, i.e. it
-// fetches global chunk (l & 7) ^ f(row); per lane only the row / chunk part of
-// the offset is kept, the K step's byte offset goes in the scalar offset.
+// instruction fills LDS slot (l & 3) of row (l >> 2) of a 16-row block, i.e.
+// it fetches global chunk (l & 3) ^ f(row); per lane only the row / chunk part
+// of the offset is kept, the K step's byte offset goes in the scalar offset.
 template <typename C>
 __device__ __forceinline__ void gemm_copy_stage(char* smem, __amdgpu_buffer_rsrc_t ra,
                                                 __amdgpu_buffer_rsrc_t rb, const int* a_voff,
                                                 const int* b_voff, const int* a_kc,
                                                 const int* b_kc, int kbase, int stage, int wave,
                                                 int K) {
-  char* sa = smem + stage * C::A_STAGE + wave * C::A_LOADS * 8 * C::ROWB;
-  char* sb = smem + C::B_BASE + stage * C::B_STAGE + wave * C::B_LOADS * 8 * C::ROWB;
+  char* sa = smem + stage * C::A_STAGE + wave * C::A_LOADS * 1024;
+  char* sb = smem + C::B_BASE + stage * C::B_STAGE + wave * C::B_LOADS * 1024;
   if (kbase + kGemmBK <= K) {   // no chunk of this step lies past K
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 8 * C::ROWB), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 1024), 16,
                                                a_voff[i], kbase * 2, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 8 * C::ROWB), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 1024), 16,
                                                b_voff[i], kbase * 2, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 8 * C::ROWB), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 1024), 16,
                                                kbase + a_kc[i] < K ? a_voff[i] : kOutOfRange,
                                                kbase * 2, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 8 * C::ROWB), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + i * 1024), 16,
                                                kbase + b_kc[i] < K ? b_voff[i] : kOutOfRange,
                                                kbase * 2, 0, 0);
   }
@@ -224,19 +250,19 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
   const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.M - m0, BM, g.lda * 2);
   const __amdgpu_buffer_rsrc_t rb = rows_rsrc(g.B, n0, g.b_rows - n0, BN, g.ldb * 2);
 
-  const int lrow = lane >> 3;
-  const int lslot = lane & 7;
+  const int lrow = lane / C::CPR;
+  const int lslot = lane % C::CPR;
   int a_voff[C::A_LOADS], b_voff[C::B_LOADS], a_kc[C::A_LOADS], b_kc[C::B_LOADS];
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
-    const int r = (wave * C::A_LOADS + i) * 8 + lrow;
-    a_kc[i] = (lslot ^ lds_swz(r)) * 8;
+    const int r = (wave * C::A_LOADS + i) * C::ROWS_PER_COPY + lrow;
+    a_kc[i] = (lslot ^ lds_swz<C::CPR>(r)) * 8;
     a_voff[i] = static_cast<int>((static_cast<int64_t>(r) * g.lda + a_kc[i]) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i) {
-    const int r = (wave * C::B_LOADS + i) * 8 + lrow;
-    b_kc[i] = (lslot ^ lds_swz(r)) * 8;
+    const int r = (wave * C::B_LOADS + i) * C::ROWS_PER_COPY + lrow;
+    b_kc[i] = (lslot ^ lds_swz<C::CPR>(r)) * 8;
     b_voff[i] = static_cast<int>((static_cast<int64_t>(r) * g.ldb + b_kc[i]) * 2);
   }
 
@@ -257,43 +283,60 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int r = wm * C::WM + i * 32 + frag_row;
-    a_off[i] = r * C::ROWB + ((frag_half ^ lds_swz(r)) << 4);
+    a_off[i] = r * C::ROWB + ((frag_half ^ lds_swz<C::CPR>(r)) << 4);
   }
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) {
     const int r = wn * C::WN + j * 32 + frag_row;
-    b_off[j] = C::B_BASE + r * C::ROWB + ((frag_half ^ lds_swz(r)) << 4);
+    b_off[j] = C::B_BASE + r * C::ROWB + ((frag_half ^ lds_swz<C::CPR>(r)) << 4);
   }
   bf16x8_t fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  static_assert(kGemmBK == 32 || kGemmBK == 64, "two or four 16-wide k slices per step");
+  constexpr int AHEAD = kGemmStages - 1;   // steps in flight ahead of the one computed
 
+  // Prologue: steps kb .. kb + AHEAD - 1 in flight, then step kb landed.
+#pragma unroll
+  for (int s = 0; s < AHEAD; ++s) {
+    if (kb + s < ke) {
+      gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
+                         __builtin_amdgcn_readfirstlane((kb + s) * kGemmBK), s, wave, g.K);
+    }
+  }
   if (kb < ke) {
-    gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
-                       __builtin_amdgcn_readfirstlane(kb * kGemmBK), 0, wave, g.K);
-    wait_lds_copies();
+    if (kb + AHEAD <= ke) wait_copies<(AHEAD - 1) * C::LOADS>(); else wait_copies<0>();
     __syncthreads();
     gemm_load_frags<C, 0>(smem, a_off, b_off, 0, fa0, fb0);
   }
   for (int ks = kb; ks < ke; ++ks) {
-    const int cur = __builtin_amdgcn_readfirstlane((ks - kb) & 1);
-    const int cur_bytes = cur * C::A_STAGE, nxt_bytes = (cur ^ 1) * C::A_STAGE;
-    const bool more = ks + 1 < ke;
-    if (more) {
+    const int t = ks - kb;
+    const int cur_bytes = __builtin_amdgcn_readfirstlane((t % kGemmStages) * C::A_STAGE);
+    const int nxt_bytes = __builtin_amdgcn_readfirstlane(((t + 1) % kGemmStages) * C::A_STAGE);
+    // the stage that step ks - 1 used is free (everyone passed the barrier
+    // after reading it): refill it with step ks + AHEAD
+    if (ks + AHEAD < ke) {
       gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
-                         __builtin_amdgcn_readfirstlane((ks + 1) * kGemmBK), cur ^ 1, wave, g.K);
+                         __builtin_amdgcn_readfirstlane((ks + AHEAD) * kGemmBK),
+                         __builtin_amdgcn_readfirstlane((t + AHEAD) % kGemmStages), wave, g.K);
     }
     gemm_load_frags<C, 1>(smem, a_off, b_off, cur_bytes, fa1, fb1);
     gemm_mfma_slice<C>(acc, fa0, fb0);
     gemm_interleave_hint<C>();
-    gemm_load_frags<C, 2>(smem, a_off, b_off, cur_bytes, fa0, fb0);
+    if constexpr (kGemmBK == 64) {
+      gemm_load_frags<C, 2>(smem, a_off, b_off, cur_bytes, fa0, fb0);
+      gemm_mfma_slice<C>(acc, fa1, fb1);
+      gemm_interleave_hint<C>();
+      gemm_load_frags<C, 3>(smem, a_off, b_off, cur_bytes, fa1, fb1);
+      gemm_mfma_slice<C>(acc, fa0, fb0);
+      gemm_interleave_hint<C>();
+    }
     gemm_mfma_slice<C>(acc, fa1, fb1);
-    gemm_interleave_hint<C>();
-    gemm_load_frags<C, 3>(smem, a_off, b_off, cur_bytes, fa1, fb1);
-    gemm_mfma_slice<C>(acc, fa0, fb0);
-    gemm_interleave_hint<C>();
-    gemm_mfma_slice<C>(acc, fa1, fb1);
-    wait_lds_copies();
-    __syncthreads();   // next stage landed; this stage is free for the copy after next
-    if (more) gemm_load_frags<C, 0>(smem, a_off, b_off, nxt_bytes, fa0, fb0);
+    if (ks + 1 < ke) {
+      // step ks + 1 landed: the copies issued after it (up to AHEAD - 1 steps)
+      // may still be in flight
+      if (ks + AHEAD < ke) wait_copies<(AHEAD - 1) * C::LOADS>(); else wait_copies<0>();
+      __syncthreads();
+      gemm_load_frags<C, 0>(smem, a_off, b_off, nxt_bytes, fa0, fb0);
+    }
   }
   AccCoord ac{wm * C::WM, wn * C::WN, lane};
   epi.template run<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, split, g,

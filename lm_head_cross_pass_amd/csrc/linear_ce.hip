@@ -79,11 +79,9 @@ struct EpiBf16 {
 
 enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToBf16 = 2, kDwStoreBf16 = 3, kDwAddBf16 = 4 };
 
-// Step 6: grad_weight accumulation. The middle chunks of the fp32 mode add
-// with buffer_atomic_add_f32, which returns nothing: the read-modify-write of
-// the fp32 accumulator happens in L2 while the workgroup moves on. Each
-// element has exactly one writer per launch and the launches are ordered, so
-// the result is the same as a plain read-modify-write, bit for bit.
+// Step 6: grad_weight accumulation. Read-modify-write epilogues issue all the
+// reads of an accumulator column before any add, so the memory latency is paid
+// once per column (this measured faster than fire-and-forget buffer atomics).
 struct EpiDw {
   float* acc32;     // [V][ld] fp32 accumulator ('fp32' mode)
   uint16_t* out16;  // [V][ld] bf16 grad_weight
@@ -98,27 +96,47 @@ struct EpiDw {
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + ac.col(j);
       if (col >= g.N) continue;
+      if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToBf16 || MODE == kDwAddBf16) {
+        // read-modify-write: all FM x 16 reads of this column first, so their
+        // latency is paid once per column instead of once per element
+        float old[FM * 16];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int e = ac.row(i, r) * ldi + col;   // tile-local row; rows >= M are dropped
-          const float v = acc[i][j][r];
-          if constexpr (MODE == kDwStoreF32) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r32, e * 4, 0, 0);
-          } else if constexpr (MODE == kDwAddF32) {
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r32, e * 4, 0, 0);
-          } else if constexpr (MODE == kDwAddF32ToBf16) {
-            const float o = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r32, e * 4, 0, 0));
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o + v), r16, e * 2, 0, 0);
-          } else if constexpr (MODE == kDwStoreBf16) {
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r16, e * 2, 0, 0);
-          } else {
-            const uint16_t o = __builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(bf16_bits_to_f32(o) + v), r16,
-                                                  e * 2, 0, 0);
+          for (int r = 0; r < 16; ++r) {
+            const int e = ac.row(i, r) * ldi + col;
+            if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToBf16) {
+              old[i * 16 + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r32, e * 4, 0, 0));
+            } else {
+              old[i * 16 + r] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0));
+            }
           }
-        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = ac.row(i, r) * ldi + col;
+            const float v = old[i * 16 + r] + acc[i][j][r];
+            if constexpr (MODE == kDwAddF32) {
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r32, e * 4, 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r16, e * 2, 0, 0);
+            }
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = ac.row(i, r) * ldi + col;   // tile-local row; rows >= M are dropped
+            const float v = acc[i][j][r];
+            if constexpr (MODE == kDwStoreF32) {
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r32, e * 4, 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r16, e * 2, 0, 0);
+            }
+          }
+      }
     }
   }
 
@@ -226,10 +244,10 @@ int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream
 }
 
 // The large tile when it yields at least one workgroup per CU of the chip
-// (256 CUs), else the small one.
-int pick_tile(int64_t M, int64_t N) {
+// (256 CUs), possibly with up to `max_split` K splits, else the small one.
+int pick_tile(int64_t M, int64_t N, int max_split = 1) {
   const int64_t big = ((M + kTileL - 1) / kTileL) * ((N + kTileL - 1) / kTileL);
-  return big >= 256 ? kTileL : kTileS;
+  return big * max_split >= 256 ? kTileL : kTileS;
 }
 
 // C[M, N] = A[M, K] B[N, K]^T where only the first b_rows rows of B exist
@@ -268,7 +286,7 @@ int transpose_pad(const uint16_t* src, int64_t ld_src, int R, int Cs, uint16_t* 
 // K splits of the grad_inputs product: enough (split, tile) pairs to give every
 // CU its resident workgroups, but at least 4 K steps per split.
 int dx_ksplit(int64_t C, int64_t D, int64_t ldv) {
-  const int tile = pick_tile(C, D);
+  const int tile = pick_tile(C, D, 2);
   const int64_t tiles = ((C + tile - 1) / tile) * ((D + tile - 1) / tile);
   const int64_t slots = tile == kTileL ? 256 : 512;
   const int64_t ksteps = ldv / kGemmBK;
@@ -382,7 +400,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
     if (st != LMX_OK) return st;
     // 5. grad_inputs rows
     {
-      const int tile = pick_tile(p.chunk, D);   // the tile the workspace was sized for
+      const int tile = pick_tile(p.chunk, D, 2);   // the tile the workspace was sized for
       GemmShape g = make_shape(z, ldv, wt, ldv, rows, D, D, static_cast<int>(ldv),
                                static_cast<int>(wl.ksplit), tile);
       EpiBf16 e{p.grad_x + r0 * p.D, p.D, dxp, p.D};
