@@ -51,8 +51,9 @@ def source_digest(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(counter_file: str, digest: str):
-    """HBM bytes per launch from a committed counter summary, if it matches the source."""
+def stored_traffic(counter_file: str, digest: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per call) from a committed counter summary, if it
+    matches the current source."""
     path = os.path.join(PROFILES, counter_file)
     if not os.path.exists(path):
         return None
@@ -61,9 +62,9 @@ def stored_traffic(counter_file: str, digest: str):
         if "=" in ln and not ln.lstrip().startswith("#"):
             k, v = ln.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != digest or "hbm_bytes_per_launch" not in vals:
+    if vals.get("source_digest") != digest or key not in vals:
         return None
-    return float(vals["hbm_bytes_per_launch"])
+    return float(vals[key])
 
 
 def main() -> int:
@@ -197,10 +198,13 @@ def main() -> int:
     if "linear" in legs:
         flops = 6.0 * lin_w.BT * lin_w.V * lin_w.D
         tf = flops / (lin_ms * 1e-3) / 1e12
+        lin_traffic = stored_traffic("linear_ce_bt16384_d4096_v128256_c2048.counters.txt",
+                                     source_digest("gemm.h", "linear_ce.hip", "ce.hip", "common.h"),
+                                     "hbm_bytes_per_call")
         lin = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(lin_ms, 3),
                "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": lin_traffic,
                             "algorithmic_flops_per_call": flops,
                             "kernel": "whole linear_ce call (gemm_nt_kernel x3 per chunk + CE)"}}
         # 'weight' accumulation, timed on its own
@@ -243,18 +247,21 @@ def main() -> int:
     if not args.no_cpu and "ce" in legs:
         import oracle
         del copies
-        rows = 2048
-        torch.manual_seed(0)
-        sel = torch.arange(rows)
-        log(f"cpu_baseline: fp64 oracle on {rows} rows of {ce_w.name}")
-        t0 = time.perf_counter()
-        oracle.cross_entropy(logits_h[sel], target_h[sel], -100, "sum", 0.0)
-        dt = time.perf_counter() - t0
+        # blocks of 2048 rows, in order, until about 20 s of host work or all rows
+        blk, rows, dt = 2048, 0, 0.0
+        log(f"cpu_baseline: fp64 oracle on row blocks of {ce_w.name}")
+        while rows < ce_w.B and dt < 20.0:
+            sel = slice(rows, min(rows + blk, ce_w.B))
+            t0 = time.perf_counter()
+            oracle.cross_entropy(logits_h[sel], target_h[sel], -100, "sum", 0.0)
+            dt += time.perf_counter() - t0
+            rows = sel.stop
         sb = 2 * rows * ce_w.V * 2 + 8 * rows
         line["cpu_baseline"] = {"value": round(sb / dt / 1e9, 3), "unit": "GB/s",
                                 "cores": torch.get_num_threads(), "kind": "oracle",
                                 "sample": f"first {rows} of {ce_w.B} rows of the CE workload "
-                                          f"(loss and gradient, fp64), {dt:.1f} s"}
+                                          f"in blocks of {blk} (loss and gradient, fp64), "
+                                          f"{dt:.1f} s"}
     print(json.dumps(line), flush=True)
     return 0
 
