@@ -228,7 +228,32 @@ __global__ __launch_bounds__(1024) void ce_count_kernel(const int64_t* target, i
   }
 }
 
+// Hides a lane-index value from loop-invariant code motion, so the per-chunk
+// offsets derived from it are recomputed where they are used instead of being
+// held in registers across the row loop.
+__device__ __forceinline__ int launder_int(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// First valid row at or after `row` in steps of `stride`; the ignored rows
+// passed over get a zero loss term and (with a gradient) a zero gradient row.
+template <typename T, int THREADS>
+__device__ __forceinline__ int64_t next_valid_row(const CeParams& p, int64_t row, int64_t stride,
+                                                  bool want_grad) {
+  for (; row < p.B; row += stride) {
+    if (row_is_valid(p.target[row], p)) break;
+    if (threadIdx.x == 0) p.row_loss[row] = 0.f;
+    if (want_grad) zero_row<T, THREADS>(p, row);
+  }
+  return row;
+}
+
 // Register-resident rows: THREADS x CPT chunks of 16 B must cover a row.
+// While the gradient of a row is written, the chunks of the workgroup's next
+// valid row are loaded into the registers just freed, so each row's loads
+// overlap the previous row's stores and arithmetic. (After the last row the
+// loads go to an empty buffer resource: they return zeros and touch no memory.)
 template <typename T, int THREADS, int CPT>
 __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
   constexpr int EPC = Elem<T>::kPerChunk;
@@ -241,24 +266,27 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
   const bool want_grad = p.grad != nullptr;
   const uintptr_t gbase = want_grad ? reinterpret_cast<uintptr_t>(p.grad) : base;
   const int V = static_cast<int>(p.V);
-  int par = 0;  // LDS slot parity; flips once per valid row (each has one barrier)
-  for (int64_t row = blockIdx.x; row < p.B; row += gridDim.x) {
+  const int64_t stride = gridDim.x;
+  int par = 0;        // LDS slot parity; flips once per valid row (each has one barrier)
+  int64_t row = next_valid_row<T, THREADS>(p, blockIdx.x, stride, want_grad);
+  if (row >= p.B) return;
+  u32x4 d[CPT];
+  {
+    const RowView r0 = row_view<T>(base, gbase, row, p.V, p.ld);
+    const int lt = launder_int(tid);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) d[k] = load_chunk(r0, lt + k * THREADS);
+  }
+  while (row < p.B) {
     const int64_t t = p.target[row];
-    if (!row_is_valid(t, p)) {
-      if (tid == 0) p.row_loss[row] = 0.f;
-      if (want_grad) zero_row<T, THREADS>(p, row);
-      continue;
-    }
     const RowView r = row_view<T>(base, gbase, row, p.V, p.ld);
     if (tid == 0) {
       sxt[par] = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.ld + t) * sizeof(T));
     }
-    u32x4 d[CPT];
+    {
+      const int lt = launder_int(tid);
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int ci = tid + k * THREADS;
-      d[k] = load_chunk(r, ci);
-      mask_edges<T>(d[k], ci, r, V);
+      for (int k = 0; k < CPT; ++k) mask_edges<T>(d[k], lt + k * THREADS, r, V);
     }
     // sweep 1: thread max, then the thread's sum of exp(x - max)
     float m = -kInf;
@@ -288,7 +316,22 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
     const float xt = sxt[par];
     par ^= 1;
     if (tid == 0) p.row_loss[row] = (m - xt) + log2s * kLn2 + p.z * lse * lse;
-    if (!want_grad) continue;
+    // the workgroup's next valid row, whose chunks are loaded below
+    const int64_t nrow = next_valid_row<T, THREADS>(p, row + stride, stride, want_grad);
+    RowView rn = r;
+    if (nrow < p.B) {
+      rn = row_view<T>(base, gbase, nrow, p.V, p.ld);
+    } else {
+      rn.in = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, 0,
+                                                kRawBufferFlags);
+    }
+    if (!want_grad) {
+      const int lp = launder_int(tid);
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) d[k] = load_chunk(rn, lp + k * THREADS);
+      row = nrow;
+      continue;
+    }
     // sweep 2: gradient from the registers
     const float c = scale * (1.f + 2.f * p.z * lse);
     const int tpos = r.lead + static_cast<int>(t);
@@ -300,9 +343,10 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
     const float mul = fold ? 1.f : c;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) launder(d[k]);
+    const int lg = launder_int(tid);
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      const int ci = tid + k * THREADS;
+      const int ci = lg + k * THREADS;
       float x[EPC];
       Elem<T>::unpack(d[k], x);
       float gv[EPC];
@@ -318,7 +362,12 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
         for (int e = 0; e < EPC; ++e) if (e == et) gv[e] -= scale;
       }
       store_chunk<T>(r, ci, V, gv);
+      d[k] = load_chunk(rn, ci);
+      // keep chunk order: hoisting the next row's loads above this row's
+      // remaining chunks would hold both rows in registers
+      __builtin_amdgcn_sched_barrier(0);
     }
+    row = nrow;
   }
 }
 
