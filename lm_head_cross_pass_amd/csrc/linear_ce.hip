@@ -227,18 +227,20 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* p, int64_t n) {
 
 // ------------------------------------------------------------------ host helpers
 
-template <typename Epi>
+// SCHED selects the main loop's schedule hints for the large tile (see
+// gemm_interleave_hint); the small tile always uses schedule 0.
+template <int SCHED, typename Epi>
 int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream) {
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   if (tile == kTileL) {
     constexpr int threads = GemmCfg<kTileL, kTileL>::THREADS;
-    hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi>), dim3(blocks), dim3(threads), 0,
-                       stream, g, epi);
+    hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi, SCHED>), dim3(blocks),
+                       dim3(threads), 0, stream, g, epi);
   } else {
     constexpr int threads = GemmCfg<kTileS, kTileS>::THREADS;
-    hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi>), dim3(blocks), dim3(threads), 0,
-                       stream, g, epi);
+    hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi, 0>), dim3(blocks), dim3(threads),
+                       0, stream, g, epi);
   }
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
@@ -375,7 +377,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       const int tile = pick_tile(rows, ldv);
       GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
       EpiBf16 e{z, ldv, nullptr, 0};
-      st = launch_gemm(g, tile, e, stream);
+      st = launch_gemm<1>(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
     // 3. cross-entropy of the chunk rows, G written over Z, loss terms
@@ -404,7 +406,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       GemmShape g = make_shape(z, ldv, wt, ldv, rows, D, D, static_cast<int>(ldv),
                                static_cast<int>(wl.ksplit), tile);
       EpiBf16 e{p.grad_x + r0 * p.D, p.D, dxp, p.D};
-      st = launch_gemm(g, tile, e, stream);
+      st = launch_gemm<1>(g, tile, e, stream);
       if (st != LMX_OK) return st;
       if (g.ksplit > 1) {
         const int64_t total = static_cast<int64_t>(rows) * D / 4;
@@ -426,7 +428,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       const int tile = pick_tile(V, D);
       GemmShape g = make_shape(gt, ldc, xt, ldc, V, D, D, static_cast<int>(ldc), 1, tile);
       EpiDw e{dw, p.grad_w, p.D, mode};
-      st = launch_gemm(g, tile, e, stream);
+      st = launch_gemm<1>(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
   }
