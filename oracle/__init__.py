@@ -15,6 +15,10 @@ Modules:
   the same loss, and the gradients of ``inputs`` and ``weight``, plus the
   chunk-by-chunk weight-dtype accumulation (greyhound functional API page,
   ``chunked_linear_loss`` and ``chunked_linear_cross_entropy``).
+* ``oracle.rows``      -- per-row operations: ``selective_log_softmax``
+  (greyhound functional API page) and the unreduced per-row cross-entropy
+  with its vector-Jacobian product (nuvec ``FastOp`` page, ``CrossEntropy`` and
+  ``CrossEntropyVjp``).
 * ``oracle.bf16``      -- round-to-nearest-even to bfloat16, written from the
   format's definition; used only by the weight-dtype accumulation emulation.
 
@@ -25,3 +29,5 @@ reductions to library routines).
 from oracle.ce import cross_entropy, cross_entropy_rows, count_valid  # noqa: F401
 from oracle.linear_ce import linear_cross_entropy  # noqa: F401
 from oracle.bf16 import round_to_bf16  # noqa: F401
+from oracle.rows import (cross_entropy_per_row, cross_entropy_per_row_vjp,  # noqa: F401
+                         selective_log_softmax)
