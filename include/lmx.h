@@ -1,7 +1,7 @@
 /*
  * lmx.h -- C ABI of liblmx.so, large-vocabulary cross-entropy on MI355X (gfx950).
  *
- * Two operations, both following the greyhound functional API page:
+ * Two operations following the greyhound functional API page:
  *
  *   ce_fwd_bwd  -- cross-entropy over materialized logits [B, V]: the reduced
  *                  loss and the logits gradient in one streaming pass
@@ -11,6 +11,16 @@
  *                  grad_inputs / grad_weight accumulated chunk by chunk without
  *                  materializing the full logits (page entries
  *                  "chunked_linear_loss" and "chunked_linear_cross_entropy").
+ *
+ * and three per-row operations on materialized logits:
+ *
+ *   selective_log_softmax -- log_softmax(x_i)[index_i] per row (greyhound
+ *                  functional API page, entry "selective_log_softmax").
+ *   ce_loss_rows   -- the unreduced per-row cross-entropy lse_i - x[i, t_i]
+ *                  (nuvec FastOp page, variant "CrossEntropy").
+ *   ce_loss_rows_vjp -- its gradient for the logits given a per-row upstream
+ *                  gradient and the forward's per-row losses (nuvec FastOp
+ *                  page, variant "CrossEntropyVjp").
  *
  * Common conventions
  * ------------------
@@ -158,6 +168,69 @@ LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int d
 
 /* Rows per chunk that linear_ce uses for this chunk_size argument (resolves 0). */
 LMX_API int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size);
+
+/*
+ * selective_log_softmax -- one log-probability per row, without materializing
+ * the log-softmax.
+ *
+ * Defined by the greyhound functional API page, entry "selective_log_softmax":
+ * the equivalent of gather(log_softmax(logits, -1), -1, index), i.e. per row
+ * out_i = x[i, index_i] - lse_i, computed with fp32 accumulation.
+ *
+ *   logits      [B, V] of `dtype`, row-major, element-aligned; 1 <= V < 2^30.
+ *   index       [B] int64 in [0, V), 8-byte aligned.
+ *   out         [B] fp32 output, 4-byte aligned, not overlapping the inputs.
+ *   bad_index   one int32 on the device, set to 1 if an index lies outside
+ *               [0, V) (that row's output is 0), else 0; may be NULL.
+ *   workspace   >= ce_workspace_bytes(B, V, dtype) bytes.
+ * B = 0 enqueues nothing but is valid.
+ */
+LMX_API int selective_log_softmax(const void* logits, const int64_t* index, int64_t B,
+                                  int64_t V, int dtype, float* out, int32_t* bad_index,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ce_loss_rows -- the unreduced per-row cross-entropy.
+ *
+ * Defined by the nuvec FastOp page, variant "CrossEntropy": per row
+ * logsumexp(x_i) - x[i, t_i] in fp32. As everywhere in this library, a row
+ * whose target equals ignore_index gets 0 (the page has no ignore index: pass
+ * a value no target takes, e.g. -100, to reproduce it exactly); a valid target
+ * outside [0, V) sets *bad_target = 1 and gets 0.
+ *
+ *   logits      [B, V] of `dtype`, row-major, element-aligned; 1 <= V < 2^30.
+ *   target      [B] int64, 8-byte aligned.
+ *   loss_rows   [B] fp32 output, 4-byte aligned, not overlapping the inputs.
+ *   n_valid, bad_target as for ce_fwd_bwd (may be NULL).
+ *   workspace   >= ce_workspace_bytes(B, V, dtype) bytes.
+ */
+LMX_API int ce_loss_rows(const void* logits, const int64_t* target, int64_t B, int64_t V,
+                         int dtype, int64_t ignore_index, float* loss_rows, int64_t* n_valid,
+                         int32_t* bad_target, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * ce_loss_rows_vjp -- gradient of sum_i g_i * ce_loss_rows_i for the logits.
+ *
+ * Defined by the nuvec FastOp page, variant "CrossEntropyVjp" (inputs logits,
+ * targets, the forward's loss and the upstream gradient g): per valid row
+ *   grad[i, :] = g_i * (softmax(x_i) - onehot(t_i)),
+ * with the row's lse taken from the forward as loss_rows_i + x[i, t_i], so the
+ * call is a single read of the logits and a single write of the gradient.
+ * Ignored rows, and rows whose target lies outside [0, V), get zero rows.
+ *
+ *   logits      [B, V] of `dtype`, row-major, element-aligned; 1 <= V < 2^30.
+ *   target      [B] int64, 8-byte aligned.
+ *   loss_rows   [B] fp32: ce_loss_rows of the same logits and targets.
+ *   g           [B] fp32 upstream gradient per row.
+ *   grad_logits [B, V] of `dtype`; may be exactly `logits` (in place), any
+ *               other overlap with an input is LMX_ERR_ALIAS; its address must
+ *               equal that of `logits` modulo 16.
+ * No workspace.
+ */
+LMX_API int ce_loss_rows_vjp(const void* logits, const int64_t* target, const float* loss_rows,
+                             const float* g, void* grad_logits, int64_t B, int64_t V, int dtype,
+                             int64_t ignore_index, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 LMX_API const char* lmx_status_string(int status);

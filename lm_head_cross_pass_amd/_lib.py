@@ -41,6 +41,9 @@ _SIGNATURES = {
     "linear_ce_chunk_rows": (_i64, [_i64, _i64, _i64]),
     "lmx_status_string": (ctypes.c_char_p, [_i32]),
     "lmx_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "selective_log_softmax": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "ce_loss_rows": (_i32, [_vp, _vp, _i64, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ce_loss_rows_vjp": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp]),
 }
 
 _lib = None
@@ -117,3 +120,21 @@ def linear_ce_chunk_rows(BT, V, chunk_size) -> int:
 
 def lmx_copy(src, dst, nbytes, stream) -> int:
     return load().lmx_copy(src, dst, nbytes, stream)
+
+
+def selective_log_softmax(logits, index, B, V, dtype, out, bad_index, workspace,
+                          workspace_bytes, stream) -> int:
+    return load().selective_log_softmax(logits, index, B, V, dtype, out, bad_index, workspace,
+                                        workspace_bytes, stream)
+
+
+def ce_loss_rows(logits, target, B, V, dtype, ignore_index, loss_rows, n_valid, bad_target,
+                 workspace, workspace_bytes, stream) -> int:
+    return load().ce_loss_rows(logits, target, B, V, dtype, ignore_index, loss_rows, n_valid,
+                               bad_target, workspace, workspace_bytes, stream)
+
+
+def ce_loss_rows_vjp(logits, target, loss_rows, g, grad_logits, B, V, dtype, ignore_index,
+                     stream) -> int:
+    return load().ce_loss_rows_vjp(logits, target, loss_rows, g, grad_logits, B, V, dtype,
+                                   ignore_index, stream)

@@ -84,7 +84,7 @@ int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int
   const lmx::CeWorkspace wl = lmx::ce_workspace_layout(B);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  lmx::CeParams p;
+  lmx::CeParams p{};
   p.logits = logits;
   p.grad = grad_logits;
   p.target = target;
@@ -100,6 +100,99 @@ int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int
   p.n_valid_user = n_valid;
   p.bad_user = bad_target;
   return lmx::ce_enqueue(p, dtype, static_cast<hipStream_t>(stream));
+}
+
+// Shared checks and launch of the per-row forward entry points: the count
+// kernel (N, the out-of-range flag), then the row kernel without a gradient,
+// writing its per-row value straight into `out`.
+static int rows_forward(const void* logits, const int64_t* target, int64_t B, int64_t V,
+                        int dtype, int64_t ignore_index, int negate, float* out,
+                        int64_t* n_valid, int32_t* bad, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (workspace == nullptr) return LMX_ERR_NULL;
+  if (B > 0 && (logits == nullptr || target == nullptr || out == nullptr)) return LMX_ERR_NULL;
+  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30)) return LMX_ERR_SIZE;
+  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  const int eb = dtype == LMX_BF16 ? 2 : 4;
+  if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
+  const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
+  if (reinterpret_cast<uintptr_t>(logits) % eb != 0 ||
+      reinterpret_cast<uintptr_t>(target) % 8 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
+    return LMX_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return LMX_ERR_WORKSPACE;
+  if (overlaps(out, B * 4, logits, bytes) || overlaps(out, B * 4, target, B * 8))
+    return LMX_ERR_ALIAS;
+  const lmx::CeWorkspace wl = lmx::ce_workspace_layout(B);
+  if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
+  if (B == 0) return LMX_OK;
+  lmx::CeParams p{};
+  p.logits = logits;
+  p.grad = nullptr;
+  p.target = target;
+  p.B = B;
+  p.V = V;
+  p.ld = V;
+  p.ignore_index = ignore_index;
+  p.z = 0.f;
+  p.reduction = LMX_SUM;
+  p.n_valid_ws = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + wl.n_valid_off);
+  p.row_loss = out;
+  p.n_valid_user = n_valid;
+  p.bad_user = bad;
+  p.negate = negate;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int r = lmx::count_enqueue(target, B, V, ignore_index, p.n_valid_ws, n_valid, bad, st);
+  if (r != LMX_OK) return r;
+  return lmx::ce_rows_enqueue(p, dtype, st);
+}
+
+int selective_log_softmax(const void* logits, const int64_t* index, int64_t B, int64_t V,
+                          int dtype, float* out, int32_t* bad_index, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  // no index is ignored: INT64_MIN is never a valid index
+  return rows_forward(logits, index, B, V, dtype, INT64_MIN, 1, out, nullptr, bad_index,
+                      workspace, workspace_bytes, stream);
+}
+
+int ce_loss_rows(const void* logits, const int64_t* target, int64_t B, int64_t V, int dtype,
+                 int64_t ignore_index, float* loss_rows, int64_t* n_valid, int32_t* bad_target,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return rows_forward(logits, target, B, V, dtype, ignore_index, 0, loss_rows, n_valid,
+                      bad_target, workspace, workspace_bytes, stream);
+}
+
+int ce_loss_rows_vjp(const void* logits, const int64_t* target, const float* loss_rows,
+                     const float* g, void* grad_logits, int64_t B, int64_t V, int dtype,
+                     int64_t ignore_index, void* stream) {
+  if (B > 0 && (logits == nullptr || target == nullptr || loss_rows == nullptr ||
+                g == nullptr || grad_logits == nullptr))
+    return LMX_ERR_NULL;
+  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30)) return LMX_ERR_SIZE;
+  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  const int eb = dtype == LMX_BF16 ? 2 : 4;
+  if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
+  const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
+  const uintptr_t pl = reinterpret_cast<uintptr_t>(logits);
+  const uintptr_t pg = reinterpret_cast<uintptr_t>(grad_logits);
+  if (pl % eb != 0 || reinterpret_cast<uintptr_t>(target) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(loss_rows) % 4 != 0 || reinterpret_cast<uintptr_t>(g) % 4 != 0)
+    return LMX_ERR_ALIGN;
+  if (pg % 16 != pl % 16) return LMX_ERR_ALIGN;
+  if (grad_logits != logits && overlaps(logits, bytes, grad_logits, bytes)) return LMX_ERR_ALIAS;
+  if (overlaps(grad_logits, bytes, target, B * 8) || overlaps(grad_logits, bytes, loss_rows, B * 4) ||
+      overlaps(grad_logits, bytes, g, B * 4))
+    return LMX_ERR_ALIAS;
+  if (B == 0) return LMX_OK;
+  lmx::VjpParams p{};
+  p.logits = logits;
+  p.grad = grad_logits;
+  p.target = target;
+  p.loss = loss_rows;
+  p.g = g;
+  p.B = B;
+  p.V = V;
+  p.ignore_index = ignore_index;
+  return lmx::ce_vjp_enqueue(p, dtype, static_cast<hipStream_t>(stream));
 }
 
 int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size) {

@@ -315,7 +315,10 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
     const float lse = m + log2s * kLn2;
     const float xt = sxt[par];
     par ^= 1;
-    if (tid == 0) p.row_loss[row] = (m - xt) + log2s * kLn2 + p.z * lse * lse;
+    if (tid == 0) {
+      const float rl = (m - xt) + log2s * kLn2 + p.z * lse * lse;
+      p.row_loss[row] = p.negate ? -rl : rl;
+    }
     // the workgroup's next valid row, whose chunks are loaded below
     const int64_t nrow = next_valid_row<T, THREADS>(p, row + stride, stride, want_grad);
     RowView rn = r;
@@ -420,7 +423,10 @@ __global__ __launch_bounds__(THREADS) void ce_rows_stream_kernel(CeParams p) {
     const float lse = m + log2s * kLn2;
     const float xt = sxt[par];
     par ^= 1;
-    if (tid == 0) p.row_loss[row] = (m - xt) + log2s * kLn2 + p.z * lse * lse;
+    if (tid == 0) {
+      const float rl = (m - xt) + log2s * kLn2 + p.z * lse * lse;
+      p.row_loss[row] = p.negate ? -rl : rl;
+    }
     if (!want_grad) continue;
     const float c = scale * (1.f + 2.f * p.z * lse);
     const int tpos = r.lead + static_cast<int>(t);
@@ -459,6 +465,76 @@ __global__ __launch_bounds__(1024) void ce_finish_kernel(const float* row_loss, 
     for (int i = 0; i < 16; ++i) tot += sd[i];
     const double n = static_cast<double>(*n_ws);
     *loss = static_cast<float>(reduction == LMX_MEAN ? tot / n : tot);
+  }
+}
+
+// Vector-Jacobian product of the unreduced per-row cross-entropy (nuvec FastOp
+// page, "CrossEntropyVjp"): grad[i, j] = g_i (exp(x_ij - lse_i) - [j == t_i]),
+// where lse_i is recovered from the forward's per-row loss as loss_i + x[i, t_i],
+// so no reduction over the row is needed: one read and one write of the
+// logits in all. One workgroup per row, walking it kVjpChunks 16-byte chunks
+// at a time; one workgroup per row also keeps the in-place case safe, since
+// x[i, t_i] is read before any part of row i is overwritten. Ignored rows (and
+// rows with a target outside [0, V)) get zeros.
+constexpr int kVjpThreads = 256;
+constexpr int kVjpPerThread = 8;
+constexpr int kVjpChunks = kVjpThreads * kVjpPerThread;
+
+template <typename T>
+__global__ __launch_bounds__(kVjpThreads) void ce_vjp_kernel(VjpParams p) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p.logits);
+  const uintptr_t gbase = reinterpret_cast<uintptr_t>(p.grad);
+  const int V = static_cast<int>(p.V);
+  const RowView r = row_view<T>(base, gbase, row, p.V, p.V);
+  const int64_t t = p.target[row];
+  if (t == p.ignore_index || t < 0 || t >= p.V) {
+    float z[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) z[e] = 0.f;
+    for (int c0 = tid; c0 < r.nch; c0 += kVjpChunks) {
+#pragma unroll
+      for (int k = 0; k < kVjpPerThread; ++k) store_chunk<T>(r, c0 + k * kVjpThreads, V, z);
+    }
+    return;
+  }
+  const float g = p.g[row];
+  const float xt = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.V + t) * sizeof(T));
+  // lse = loss + x[t] without a rounding: fp32 logits take x - lse in fp64
+  // (the float loss input then carries the only rounding), bf16 logits one fma
+  const double lse_d = static_cast<double>(p.loss[row]) + static_cast<double>(xt);
+  const float lseL = static_cast<float>(lse_d * static_cast<double>(kLog2e));
+  const int tpos = r.lead + static_cast<int>(t);
+  const int ct = tpos / EPC;
+  const int et = tpos % EPC;
+  // every thread has read x[t] (through lse) before any store of the row
+  __syncthreads();
+  for (int c0 = tid; c0 < r.nch; c0 += kVjpChunks) {
+    u32x4 d[kVjpPerThread];
+#pragma unroll
+    for (int k = 0; k < kVjpPerThread; ++k) d[k] = load_chunk(r, c0 + k * kVjpThreads);
+#pragma unroll
+    for (int k = 0; k < kVjpPerThread; ++k) {
+      const int ci = c0 + k * kVjpThreads;
+      float x[EPC], gv[EPC];
+      Elem<T>::unpack(d[k], x);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (sizeof(T) == 4) {
+          const float dx = static_cast<float>(static_cast<double>(x[e]) - lse_d);
+          gv[e] = g * exp2_fast(dx * kLog2e);
+        } else {
+          gv[e] = g * exp2_fast(__builtin_fmaf(x[e], kLog2e, -lseL));
+        }
+      }
+      if (ci == ct) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) if (e == et) gv[e] -= g;
+      }
+      store_chunk<T>(r, ci, V, gv);   // chunks past the row fall outside the resource
+    }
   }
 }
 
@@ -553,6 +629,19 @@ int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
   st = ce_rows_enqueue(p, dtype, stream);
   if (st != LMX_OK) return st;
   return finish_enqueue(p.row_loss, p.B, p.n_valid_ws, p.reduction, p.loss, stream);
+}
+
+int ce_vjp_enqueue(const VjpParams& p, int dtype, hipStream_t stream) {
+  if (p.B == 0) return LMX_OK;
+  if (p.B > INT32_MAX) return LMX_ERR_SIZE;
+  const void* fn = dtype == LMX_BF16 ? reinterpret_cast<const void*>(&ce_vjp_kernel<uint16_t>)
+                                     : reinterpret_cast<const void*>(&ce_vjp_kernel<float>);
+  VjpParams pc = p;
+  void* args[] = {&pc};
+  if (hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.B)), dim3(kVjpThreads), args, 0,
+                      stream) != hipSuccess)
+    return LMX_ERR_HIP;
+  return LMX_OK;
 }
 
 }  // namespace lmx

@@ -20,6 +20,7 @@ struct CeParams {
   float* loss;              // output scalar
   int64_t* n_valid_user;    // optional output
   int32_t* bad_user;        // optional output
+  int negate;               // row outputs x[t] - lse instead of lse - x[t] (z must be 0)
 };
 
 // N and the out-of-range flag over `target` (one workgroup, no zeroed memory needed).
@@ -38,6 +39,19 @@ int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream);
 
 // Largest number of 16-byte chunks any row touches (for kernel selection).
 int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int64_t ld, int elem_bytes);
+
+// Per-row vector-Jacobian product of the unreduced cross-entropy:
+// grad[i, :] = g[i] (softmax(x_i) - onehot(t_i)) with lse_i = loss[i] + x[i, t_i].
+struct VjpParams {
+  const void* logits;       // [B, V]
+  void* grad;               // [B, V]; may equal logits
+  const int64_t* target;    // [B]
+  const float* loss;        // [B] forward per-row losses
+  const float* g;           // [B] upstream gradient per row
+  int64_t B, V;
+  int64_t ignore_index;
+};
+int ce_vjp_enqueue(const VjpParams& p, int dtype, hipStream_t stream);
 
 // Workspace layout of ce_fwd_bwd.
 struct CeWorkspace {

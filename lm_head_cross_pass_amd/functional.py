@@ -9,10 +9,17 @@ computation runs in the library's kernels. The functions:
   logits with their gradient (upstream gradient 1);
 * ``linear_cross_entropy`` -- chunked ``inputs @ weight.T`` cross-entropy with
   gradients for inputs and weight (page entries ``chunked_linear_loss`` and
-  ``chunked_linear_cross_entropy``; ``chunk_size`` as in the former).
+  ``chunked_linear_cross_entropy``; ``chunk_size`` as in the former);
+* ``selective_log_softmax`` -- one log-probability per row (page entry
+  ``selective_log_softmax``);
+* ``cross_entropy_per_row`` -- the unreduced per-row cross-entropy whose
+  backward is the separate vector-Jacobian product call (nuvec ``FastOp``
+  page, ``CrossEntropy`` / ``CrossEntropyVjp``).
 
-The gradients are produced in the forward call (one pass); backward only
-scales them by the upstream scalar gradient.
+For the reduced losses the gradients are produced in the forward call (one
+pass) and backward only scales them by the upstream scalar gradient; the
+per-row loss instead runs its own backward pass, since its upstream gradient
+is a vector.
 """
 from __future__ import annotations
 
@@ -179,3 +186,89 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
     """Chunked linear cross-entropy with z-loss; gradients flow to inputs and weight."""
     return _LinearCrossEntropy.apply(inputs, weight, target, ignore_index, reduction,
                                      z_loss_multiplier, chunk_size, grad_weight_accum_dtype)
+
+
+def _rows_args(logits: torch.Tensor, index: torch.Tensor, what: str):
+    _require_device(logits, "logits")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [B, V] tensor")
+    if logits.dtype not in _DTYPES:
+        raise ValueError(f"unsupported logits dtype {logits.dtype}")
+    B, V = logits.shape
+    index = index.to(device=logits.device, dtype=torch.int64).contiguous()
+    if index.shape != (B,):
+        raise ValueError(f"{what} must have shape [B]")
+    return B, V, index
+
+
+def selective_log_softmax(logits: torch.Tensor, index: torch.Tensor) -> torch.Tensor:
+    """``log_softmax(logits, -1).gather(-1, index[:, None])[:, 0]`` as fp32 [B]; no autograd."""
+    B, V, index = _rows_args(logits, index, "index")
+    dev = logits.device
+    out = torch.empty(B, dtype=torch.float32, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    dtype = _DTYPES[logits.dtype]
+    ws = _workspace(_lib.ce_workspace_bytes(B, V, dtype), dev)
+    with torch.cuda.device(dev):
+        st = _lib.selective_log_softmax(logits.data_ptr(), index.data_ptr(), B, V, dtype,
+                                        out.data_ptr(), bad.data_ptr(), ws.data_ptr(),
+                                        ws.numel(), _stream_handle(dev))
+    _lib.check("selective_log_softmax", st)
+    return out
+
+
+def ce_loss_rows(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100):
+    """One library call: (per-row losses fp32 [B], n_valid, bad_target)."""
+    B, V, target = _rows_args(logits, target, "target")
+    dev = logits.device
+    out = torch.empty(B, dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    bad = torch.empty((), dtype=torch.int32, device=dev)
+    dtype = _DTYPES[logits.dtype]
+    ws = _workspace(_lib.ce_workspace_bytes(B, V, dtype), dev)
+    with torch.cuda.device(dev):
+        st = _lib.ce_loss_rows(logits.data_ptr(), target.data_ptr(), B, V, dtype,
+                               int(ignore_index), out.data_ptr(), n_valid.data_ptr(),
+                               bad.data_ptr(), ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _lib.check("ce_loss_rows", st)
+    return out, n_valid, bad
+
+
+def ce_loss_rows_vjp(logits: torch.Tensor, target: torch.Tensor, loss_rows: torch.Tensor,
+                     g: torch.Tensor, ignore_index: int = -100,
+                     in_place: bool = False) -> torch.Tensor:
+    """One library call: d(sum_i g_i loss_i)/d(logits), in the logits dtype."""
+    B, V, target = _rows_args(logits, target, "target")
+    dev = logits.device
+    loss_rows = loss_rows.to(device=dev, dtype=torch.float32).contiguous()
+    g = g.to(device=dev, dtype=torch.float32).contiguous()
+    if loss_rows.shape != (B,) or g.shape != (B,):
+        raise ValueError("loss_rows and g must have shape [B]")
+    grad = logits if in_place else torch.empty_like(logits)
+    with torch.cuda.device(dev):
+        st = _lib.ce_loss_rows_vjp(logits.data_ptr(), target.data_ptr(), loss_rows.data_ptr(),
+                                   g.data_ptr(), grad.data_ptr(), B, V, _DTYPES[logits.dtype],
+                                   int(ignore_index), _stream_handle(dev))
+    _lib.check("ce_loss_rows_vjp", st)
+    return grad
+
+
+class _CrossEntropyPerRow(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, target, ignore_index):
+        loss, _, _ = ce_loss_rows(logits.detach(), target, ignore_index)
+        ctx.ignore_index = ignore_index
+        ctx.save_for_backward(logits.detach(), target, loss)
+        return loss
+
+    @staticmethod
+    def backward(ctx, g):
+        logits, target, loss = ctx.saved_tensors
+        return ce_loss_rows_vjp(logits, target, loss, g, ctx.ignore_index), None, None
+
+
+def cross_entropy_per_row(logits: torch.Tensor, target: torch.Tensor,
+                          ignore_index: int = -100) -> torch.Tensor:
+    """Unreduced cross-entropy ``logsumexp(x_i) - x_i[t_i]`` per row (fp32 [B], 0 where
+    ignored); its backward is one ``ce_loss_rows_vjp`` pass over the logits."""
+    return _CrossEntropyPerRow.apply(logits, target, ignore_index)

@@ -30,7 +30,8 @@ def test_every_declared_function_is_exported():
     names = _lib.header_functions()
     assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "linear_ce",
                           "linear_ce_workspace_bytes", "linear_ce_chunk_rows",
-                          "lmx_status_string", "lmx_copy"}
+                          "lmx_status_string", "lmx_copy", "selective_log_softmax",
+                          "ce_loss_rows", "ce_loss_rows_vjp"}
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -156,3 +157,63 @@ def test_copy_argument_errors():
     assert _lib.lmx_copy(A + 8, A + (1 << 34), 16, None) == _lib.LMX_ERR_ALIGN
     assert _lib.lmx_copy(A, A + 16, 64, None) == _lib.LMX_ERR_ALIAS
     assert _lib.lmx_copy(A, A, 0, None) == _lib.LMX_OK
+
+
+def _rows(fn, **kw):
+    args = dict(logits=A, index=A + (2 << 34), B=8, V=1000, dtype=F32, ignore=-100,
+                out=A + (3 << 34), n=None, bad=None, ws=A + (4 << 34), wsb=WS, stream=None)
+    args.update(kw)
+    if fn == "selective_log_softmax":
+        return _lib.selective_log_softmax(args["logits"], args["index"], args["B"], args["V"],
+                                          args["dtype"], args["out"], args["bad"], args["ws"],
+                                          args["wsb"], args["stream"])
+    return _lib.ce_loss_rows(args["logits"], args["index"], args["B"], args["V"], args["dtype"],
+                             args["ignore"], args["out"], args["n"], args["bad"], args["ws"],
+                             args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", ("selective_log_softmax", "ce_loss_rows"))
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), _lib.LMX_ERR_NULL),
+    (dict(out=None), _lib.LMX_ERR_NULL),
+    (dict(logits=None), _lib.LMX_ERR_NULL),
+    (dict(B=-1), _lib.LMX_ERR_SIZE),
+    (dict(V=0), _lib.LMX_ERR_SIZE),
+    (dict(V=1 << 30), _lib.LMX_ERR_SIZE),
+    (dict(dtype=2), _lib.LMX_ERR_ENUM),
+    (dict(logits=A + 2), _lib.LMX_ERR_ALIGN),
+    (dict(index=A + (2 << 34) + 4), _lib.LMX_ERR_ALIGN),
+    (dict(out=A + (3 << 34) + 2), _lib.LMX_ERR_ALIGN),
+    (dict(ws=A + 64), _lib.LMX_ERR_WORKSPACE),
+    (dict(wsb=16), _lib.LMX_ERR_WORKSPACE),
+    (dict(out=A + 64), _lib.LMX_ERR_ALIAS),                 # inside the logits
+    (dict(B=0, logits=None, index=None, out=None), _lib.LMX_OK),
+])
+def test_row_forward_argument_errors(fn, kw, status):
+    assert _rows(fn, **kw) == status
+
+
+def _vjp(**kw):
+    args = dict(logits=A, target=A + (2 << 34), loss=A + (3 << 34), g=A + (5 << 34),
+                grad=A + (1 << 34), B=8, V=1000, dtype=F32, ignore=-100, stream=None)
+    args.update(kw)
+    return _lib.ce_loss_rows_vjp(args["logits"], args["target"], args["loss"], args["g"],
+                                 args["grad"], args["B"], args["V"], args["dtype"],
+                                 args["ignore"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), _lib.LMX_ERR_NULL),
+    (dict(loss=None), _lib.LMX_ERR_NULL),
+    (dict(grad=None), _lib.LMX_ERR_NULL),
+    (dict(B=-1), _lib.LMX_ERR_SIZE),
+    (dict(V=0), _lib.LMX_ERR_SIZE),
+    (dict(dtype=5), _lib.LMX_ERR_ENUM),
+    (dict(loss=A + (3 << 34) + 2), _lib.LMX_ERR_ALIGN),
+    (dict(grad=A + (1 << 34) + 4), _lib.LMX_ERR_ALIGN),     # differs from logits modulo 16
+    (dict(grad=A + 4000 * 4), _lib.LMX_ERR_ALIAS),          # overlaps logits, not equal
+    (dict(g=A + (1 << 34) + 64), _lib.LMX_ERR_ALIAS),       # g inside the gradient
+    (dict(B=0, logits=None, target=None, loss=None, g=None, grad=None), _lib.LMX_OK),
+])
+def test_vjp_argument_errors(kw, status):
+    assert _vjp(**kw) == status

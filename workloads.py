@@ -177,3 +177,9 @@ def small_linear_ce(BT: int, D: int, V: int, dtype=torch.bfloat16, sigma_x: floa
     x = _normal_rows(g, BT, D, sigma_x, dtype)
     wt = _normal_rows(g, V, D, sigma_w, dtype)
     return x, wt, target
+
+
+def row_upstream(B: int, seed: int = 0) -> torch.Tensor:
+    """A per-row upstream gradient g [B] fp32 ~ N(0, 1) (for the per-row VJP tests)."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    return torch.randn(B, generator=g, dtype=torch.float32)
