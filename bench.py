@@ -16,10 +16,12 @@ one read of the logits, one write of the gradient, the int64 targets) with its
 roofline against the 8 TB/s HBM peak, and the linear-CE leg under
 ``linear_ce`` (TFLOP/s of the three matmuls, 6 BT V D, against the 2.5 PFLOP/s
 dense bf16 MFMA peak), plus its 'weight'-accumulation variant timed on its own.
-``cpu_baseline`` is the fp64 oracle timed on the host on a bounded sample of
-the same CE workload.
+``next_rows`` times the per-row entry points on the CE leg's logits (forward-only
+reduced CE, selective_log_softmax, the unreduced per-row CE and its VJP), each
+in GB/s of its own algorithmic bytes. ``cpu_baseline`` is the fp64 oracle timed
+on the host on a bounded sample of the same CE workload.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -72,7 +74,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="ce,linear")
+    ap.add_argument("--legs", default="ce,linear,rows",
+                    help="ce, linear, rows (the per-row entry points; needs ce)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--weight-steps", type=int, default=3)
     args = ap.parse_args()
@@ -242,6 +245,63 @@ def main() -> int:
         cms = e0.elapsed_time(e1) / 3
         line["copy_ceiling"] = {"value": round(2 * nb / (cms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                 "bytes_moved": 2 * nb}
+
+    # ------------------------------------------------------------ per-row entry points
+    # forward-only reduced CE, selective_log_softmax, the unreduced per-row CE and
+    # its VJP, on the same [16384, 128256] bf16 logits (resident in HBM)
+    if "ce" in legs and "rows" in legs:
+        B, V = ce_w.B, ce_w.V
+        src, dst = copies[0], copies[1]
+        index = torch.clamp(target, min=0)
+        rl = torch.empty(B, dtype=torch.float32, device=dev)
+        lp = torch.empty(B, dtype=torch.float32, device=dev)
+        g = workloads.row_upstream(B).to(dev)
+        sp = stream.cuda_stream
+
+        def fwd_only():
+            _lib.check("ce_fwd_bwd", _lib.ce_fwd_bwd(
+                src.data_ptr(), None, target.data_ptr(), B, V, _lib.LMX_BF16, -100, _lib.LMX_SUM,
+                0.0, ce_out[0].data_ptr(), ce_out[1].data_ptr(), ce_out[2].data_ptr(),
+                ce_ws.data_ptr(), ce_ws.numel(), sp))
+
+        def sel():
+            _lib.check("selective_log_softmax", _lib.selective_log_softmax(
+                src.data_ptr(), index.data_ptr(), B, V, _lib.LMX_BF16, lp.data_ptr(),
+                ce_out[2].data_ptr(), ce_ws.data_ptr(), ce_ws.numel(), sp))
+
+        def rows_fwd():
+            _lib.check("ce_loss_rows", _lib.ce_loss_rows(
+                src.data_ptr(), target.data_ptr(), B, V, _lib.LMX_BF16, -100, rl.data_ptr(),
+                ce_out[1].data_ptr(), ce_out[2].data_ptr(), ce_ws.data_ptr(), ce_ws.numel(), sp))
+
+        def vjp():
+            _lib.check("ce_loss_rows_vjp", _lib.ce_loss_rows_vjp(
+                src.data_ptr(), target.data_ptr(), rl.data_ptr(), g.data_ptr(), dst.data_ptr(),
+                B, V, _lib.LMX_BF16, -100, sp))
+
+        read_bytes = B * V * 2 + 8 * B
+        legs_rows = (("ce_forward_only", fwd_only, read_bytes),
+                     ("selective_log_softmax", sel, read_bytes + 4 * B),
+                     ("ce_loss_rows", rows_fwd, read_bytes + 4 * B),
+                     ("ce_loss_rows_vjp", vjp, 2 * B * V * 2 + 16 * B))
+        rows_line = {"workload": ce_w.name, "unit": "GB/s", "peak": HBM_PEAK_GBPS}
+        rows_fwd()
+        for name, fn, nbytes in legs_rows:
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(10):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            rows_line[name] = {"value": round(gbps, 1), "ms_per_call": round(ms, 4),
+                               "algorithmic_bytes": nbytes, "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            log(f"{name}: {ms:.3f} ms, {gbps:.0f} GB/s")
+        line["next_rows"] = rows_line
 
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu and "ce" in legs:

@@ -254,7 +254,9 @@ __device__ __forceinline__ int64_t next_valid_row(const CeParams& p, int64_t row
 // valid row are loaded into the registers just freed, so each row's loads
 // overlap the previous row's stores and arithmetic. (After the last row the
 // loads go to an empty buffer resource: they return zeros and touch no memory.)
-template <typename T, int THREADS, int CPT>
+// GRAD: a gradient is written (p.grad != nullptr); a separate instantiation
+// for the loss-only case keeps each variant's registers to its own sweeps.
+template <typename T, int THREADS, int CPT, bool GRAD>
 __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
   constexpr int EPC = Elem<T>::kPerChunk;
   constexpr int W = THREADS / 64;
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
   const int tid = threadIdx.x;
   const float scale = reduction_scale(p);
   const uintptr_t base = reinterpret_cast<uintptr_t>(p.logits);
-  const bool want_grad = p.grad != nullptr;
+  constexpr bool want_grad = GRAD;
   const uintptr_t gbase = want_grad ? reinterpret_cast<uintptr_t>(p.grad) : base;
   const int V = static_cast<int>(p.V);
   const int64_t stride = gridDim.x;
@@ -288,26 +290,59 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) mask_edges<T>(d[k], lt + k * THREADS, r, V);
     }
-    // sweep 1: thread max, then the thread's sum of exp(x - max)
-    float m = -kInf;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      float x[EPC];
-      Elem<T>::unpack(d[k], x);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) m = fmaxf(m, x[e]);
+    // the workgroup's next valid row, whose chunks are loaded into the
+    // registers as this row's chunks are consumed
+    const int64_t nrow = next_valid_row<T, THREADS>(p, row + stride, stride, want_grad);
+    RowView rn = r;
+    if (nrow < p.B) {
+      rn = row_view<T>(base, gbase, nrow, p.V, p.ld);
+    } else {
+      rn.in = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, 0,
+                                                kRawBufferFlags);
     }
-    float s = 0.f;
+    float m = -kInf, s = 0.f;
+    if constexpr (!want_grad) {
+      // loss only: one online sweep (running max, sum rescaled when the max
+      // grows), so every chunk is consumed once and refilled at once
+      const int lp = launder_int(tid);
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) launder(d[k]);
-    if (m != -kInf) {
-      const float mL = m * kLog2e;
+      for (int k = 0; k < CPT; ++k) {
+        float x[EPC];
+        Elem<T>::unpack(d[k], x);
+        float cm = x[0];
+#pragma unroll
+        for (int e = 1; e < EPC; ++e) cm = fmaxf(cm, x[e]);
+        const float nm = fmaxf(m, cm);
+        if (nm != -kInf) {
+          s *= exp2_fast((m - nm) * kLog2e);
+          const float nmL = nm * kLog2e;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) s += shifted_exp2<T>(x[e], nm, 0.f, nmL);
+        }
+        m = nm;
+        d[k] = load_chunk(rn, lp + k * THREADS);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // sweep 1: thread max, then the thread's sum of exp(x - max)
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         float x[EPC];
         Elem<T>::unpack(d[k], x);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) s += shifted_exp2<T>(x[e], m, 0.f, mL);
+        for (int e = 0; e < EPC; ++e) m = fmaxf(m, x[e]);
+      }
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) launder(d[k]);
+      if (m != -kInf) {
+        const float mL = m * kLog2e;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          float x[EPC];
+          Elem<T>::unpack(d[k], x);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) s += shifted_exp2<T>(x[e], m, 0.f, mL);
+        }
       }
     }
     block_lse<THREADS>(m, s, sm[par], ss[par]);
@@ -319,19 +354,7 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
       const float rl = (m - xt) + log2s * kLn2 + p.z * lse * lse;
       p.row_loss[row] = p.negate ? -rl : rl;
     }
-    // the workgroup's next valid row, whose chunks are loaded below
-    const int64_t nrow = next_valid_row<T, THREADS>(p, row + stride, stride, want_grad);
-    RowView rn = r;
-    if (nrow < p.B) {
-      rn = row_view<T>(base, gbase, nrow, p.V, p.ld);
-    } else {
-      rn.in = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, 0,
-                                                kRawBufferFlags);
-    }
-    if (!want_grad) {
-      const int lp = launder_int(tid);
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) d[k] = load_chunk(rn, lp + k * THREADS);
+    if constexpr (!want_grad) {
       row = nrow;
       continue;
     }
@@ -546,18 +569,18 @@ struct RowKernel {
   int64_t capacity;  // chunks per row that fit; 0 = any (streaming)
 };
 
-template <typename T>
+template <typename T, bool G>
 const RowKernel* row_kernels(int* count) {
   static const RowKernel k[] = {
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 1>), 256, 256},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 2>), 256, 512},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 4>), 256, 1024},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 8>), 256, 2048},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 16>), 256, 4096},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13>), 512, 6656},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 16>), 512, 8192},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 12>), 1024, 12288},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 16>), 1024, 16384},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 1, G>), 256, 256},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 2, G>), 256, 512},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 4, G>), 256, 1024},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 8, G>), 256, 2048},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 16, G>), 256, 4096},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13, G>), 512, 6656},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 16, G>), 512, 8192},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 12, G>), 1024, 12288},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 16, G>), 1024, 16384},
       {reinterpret_cast<const void*>(&ce_rows_stream_kernel<T, 1024>), 1024, 0},
   };
   *count = static_cast<int>(sizeof(k) / sizeof(k[0]));
@@ -607,7 +630,10 @@ int ce_rows_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
     const int eb = dtype == LMX_BF16 ? 2 : 4;
     const int64_t need = ce_max_row_chunks(reinterpret_cast<uintptr_t>(p.logits), p.V, p.ld, eb);
     int n = 0;
-    const RowKernel* ks = dtype == LMX_BF16 ? row_kernels<uint16_t>(&n) : row_kernels<float>(&n);
+    const bool g = p.grad != nullptr;
+    const RowKernel* ks = dtype == LMX_BF16
+                              ? (g ? row_kernels<uint16_t, true>(&n) : row_kernels<uint16_t, false>(&n))
+                              : (g ? row_kernels<float, true>(&n) : row_kernels<float, false>(&n));
     const RowKernel* pick = &ks[n - 1];
     for (int i = 0; i < n; ++i) {
       if (ks[i].capacity == 0 || ks[i].capacity >= need) { pick = &ks[i]; break; }

@@ -92,8 +92,12 @@ def test_shapes_against_oracle(B, V, dtype):
         loss2, grad2, _, _, _ = _run(logits, target, red, z, in_place=True)
         assert torch.equal(grad2, grad), "in place differs from out of place"
         assert float(loss2) == float(loss)
+        # the loss-only path folds each chunk into a running max / rescaled sum
+        # (one sweep), so it matches the two-sweep value up to fp32 rounding
         loss3, g3, _, _, _ = _run(logits, target, red, z, want_grad=False)
-        assert g3 is None and float(loss3) == float(loss)
+        assert g3 is None
+        _check(logits, target, red, z, loss3, None, n, ref=ref)
+        assert float(loss3) == pytest.approx(float(loss), rel=2e-6, abs=1e-30)
 
 
 def test_misaligned_rows_and_base():
