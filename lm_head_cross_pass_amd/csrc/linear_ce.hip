@@ -6,18 +6,24 @@
 // Per call:   count valid targets (global N, needed before any gradient is
 //             scaled); W^T [D, ldv] (zero-padded) for the grad_inputs GEMM.
 // Per chunk of C rows (r0 .. r0 + C'):
-//   1. X_c^T [D, ldc]                                  transpose
+//   1. X_c^T into its columns of X^T [D, ldk]          transpose
 //   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM
 //   3. the cross-entropy row kernel on Z, in place: loss terms and
 //      G = scale ((1 + 2 z lse) softmax - onehot)      same kernel as ce_fwd_bwd
-//   4. G^T [ldv, ldc]                                  transpose
+//   4. G^T into its columns of G^T [ldv, ldk]          transpose
 //   5. grad_inputs[r0:] = G W                          MFMA GEMM (split-K if the
 //                                                      tile count cannot fill the chip)
 //   6. dW (+)= G^T X_c                                 MFMA GEMM, accumulate epilogue
 // Finally the fixed-order loss reduction. In 'fp32' accumulation dW lives in
-// an fp32 workspace and the last chunk's epilogue writes the rounded bf16
-// result; in 'weight' accumulation the bf16 grad_weight itself is updated per
-// chunk (rounded to nearest even after each chunk).
+// an fp32 workspace and the last product's epilogue writes the rounded bf16
+// result; there step 6 runs once per group of chunks (as many as 1 GiB of G^T
+// holds: two at a vocabulary of 128256 and chunks of 2048), on the group's
+// columns of G^T and X^T together (K = group ldc, ldk = group ldc; a last,
+// partial group runs on the chunks it has), which divides the passes over
+// the fp32 accumulator by the group size. In
+// 'weight' accumulation the bf16 grad_weight itself is updated per chunk
+// (rounded to nearest even after each chunk, as the accumulation mode
+// prescribes; ldk = ldc).
 //
 // The logits and G are kept in bf16 between steps, as bf16 matmuls produce
 // them; the cross-entropy of a chunk is computed in fp32 from the rounded
@@ -320,6 +326,17 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.ldc = round_up64(C, kLdcAlign);
   w.ksplit = dx_ksplit(C, D, w.ldv);
   const int64_t nchunks = BT > 0 ? (BT + C - 1) / C : 0;
+  // fp32 accumulation takes the grad_weight product of several chunks at once
+  // (K = group ldc): as many chunks as G^T of 1 GiB holds, so the fp32
+  // accumulator is read and written once per group instead of once per chunk
+  w.dw_group = 1;
+  if (accum == LMX_ACC_F32 && nchunks > 1) {
+    const int64_t per_chunk = w.ldv * w.ldc * 2;
+    int64_t gsz = (int64_t{1} << 30) / per_chunk;
+    if (gsz > nchunks) gsz = nchunks;
+    if (gsz > 1) w.dw_group = gsz;
+  }
+  w.ldk = w.dw_group * w.ldc;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -329,8 +346,8 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.n_valid_off = take(8);
   w.row_loss_off = take(static_cast<size_t>(BT) * 4);
   w.z_off = take(static_cast<size_t>(C) * w.ldv * 2);
-  w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldc * 2);
-  w.xt_off = take(static_cast<size_t>(D) * w.ldc * 2);
+  w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldk * 2);
+  w.xt_off = take(static_cast<size_t>(D) * w.ldk * 2);
   w.wt_off = take(static_cast<size_t>(D) * w.ldv * 2);
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
   w.dw_off = take(accum == LMX_ACC_F32 && nchunks > 1 ? static_cast<size_t>(V) * D * 4 : 0);
@@ -350,7 +367,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
   const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
-  const int64_t ldv = wl.ldv, ldc = wl.ldc;
+  const int64_t ldv = wl.ldv, ldc = wl.ldc, ldk = wl.ldk, grp = wl.dw_group;
 
   int st = count_enqueue(p.target, p.BT, p.V, p.ignore_index, n_ws, p.n_valid_user, p.bad_user,
                          stream);
@@ -369,8 +386,9 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
     const int rows = static_cast<int>(p.BT - r0 < p.chunk ? p.BT - r0 : p.chunk);
     const uint16_t* xc = p.x + r0 * p.D;
     const int64_t* tc = p.target + r0;
+    const int64_t slot = c % grp;   // this chunk's columns in G^T and X^T
     // 1. X_c^T
-    st = transpose_pad(xc, p.D, rows, D, xt, ldc, static_cast<int>(ldc), stream);
+    st = transpose_pad(xc, p.D, rows, D, xt + slot * ldc, ldk, static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
     // 2. logits Z = X_c W^T over all ldv columns (columns >= V read zero rows of W)
     {
@@ -398,7 +416,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       if (st != LMX_OK) return st;
     }
     // 4. G^T for the grad_weight product
-    st = transpose_pad(z, ldv, rows, V, gt, ldc, static_cast<int>(ldc), stream);
+    st = transpose_pad(z, ldv, rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
     // 5. grad_inputs rows
     {
@@ -416,17 +434,19 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
         if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
       }
     }
-    // 6. grad_weight
-    {
+    // 6. grad_weight, once per group of chunks
+    if (slot == grp - 1 || c == nchunks - 1) {
+      const int64_t gi = c / grp, ngroups = (nchunks + grp - 1) / grp;
+      const bool first = gi == 0, last = gi == ngroups - 1;
       int mode;
-      const bool first = c == 0, last = c == nchunks - 1;
       if (p.accum == LMX_ACC_F32) {
-        mode = nchunks == 1 ? kDwStoreBf16 : first ? kDwStoreF32 : last ? kDwAddF32ToBf16 : kDwAddF32;
+        mode = ngroups == 1 ? kDwStoreBf16 : first ? kDwStoreF32 : last ? kDwAddF32ToBf16 : kDwAddF32;
       } else {
         mode = first ? kDwStoreBf16 : kDwAddBf16;
       }
       const int tile = pick_tile(V, D);
-      GemmShape g = make_shape(gt, ldc, xt, ldc, V, D, D, static_cast<int>(ldc), 1, tile);
+      GemmShape g = make_shape(gt, ldk, xt, ldk, V, D, D, static_cast<int>((slot + 1) * ldc), 1,
+                               tile);
       EpiDw e{dw, p.grad_w, p.D, mode};
       st = launch_gemm<1>(g, tile, e, stream);
       if (st != LMX_OK) return st;

@@ -42,6 +42,8 @@ CASES = [
     (257, 128, 4099, 100),
     (300, 256, 8192, 0),       # default chunk size
     (1024, 64, 257, 1024),     # one chunk of 1024 rows; ksplit > 1 path
+    (256, 64, 1000, 64),       # four chunks: two paired grad_weight products
+    (250, 80, 777, 50),        # five chunks: two pairs and a last chunk alone
 ]
 
 
@@ -147,6 +149,25 @@ def test_workload_bt8192_d768_v50257_full():
     assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
     assert _rel(gx, ref["grad_inputs"]) <= 1e-2
     assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+def test_grouped_grad_weight_products_sampled():
+    """Five chunks of 2048 rows at V = 128256: fp32 accumulation groups two
+    chunks per grad_weight product (G^T of 1 GiB), so the products are a first
+    pair (fp32 store), a middle pair (read-modify-write) and the last chunk alone
+    (read-modify-write and bf16 cast); checked on sampled rows."""
+    BT, D, V, C = 5 * 2048, 64, 128256, 2048
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=200, seed=12)
+    loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, C, "fp32")
+    g = torch.Generator().manual_seed(3)
+    rows = torch.randperm(BT, generator=g)[:16].tolist()
+    vrows = torch.randperm(V, generator=g)[:16].tolist() + [int(t[rows[0]]), V - 1]
+    ref = olce.linear_cross_entropy_sampled(X, W, t, rows, vrows, -100, "mean", 1e-4,
+                                            block_rows=1024)
+    assert int(n) == BT - 200 and int(bad) == 0
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx.cpu()[rows], ref["grad_inputs_rows"]) <= 1e-2
+    assert _rel(gw.cpu()[vrows], ref["grad_weight_rows"]) <= 1e-2
 
 
 @pytest.mark.slow
