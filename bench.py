@@ -46,10 +46,17 @@ def log(msg: str) -> None:
 
 
 def source_digest(*names: str) -> str:
+    """Digest of the code of these kernel sources (comments and blank lines
+    removed), which ties a stored counter summary to the code it measured."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "lm_head_cross_pass_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "lm_head_cross_pass_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

@@ -6,9 +6,11 @@
 // values of one row of A (or of B^T).
 //
 // Work decomposition:
-// * a workgroup of 256 threads (4 waves as 2 x 2) computes a BM x BN tile,
-//   each wave a (BM/2) x (BN/2) sub-tile as a grid of 32 x 32 MFMA tiles
-//   (128 x 128 per wave at BM = BN = 256: 256 fp32 accumulators per lane);
+// * a workgroup computes a BM x BN tile: 512 threads (8 waves as 2 x 4) for
+//   256 x 256, 256 threads (4 waves as 2 x 2) for 128 x 128; each wave owns a
+//   (BM / 2) x (BN / WAVES_N) sub-tile as a grid of 32 x 32 MFMA tiles
+//   (128 x 64 per wave at 256 x 256: 128 fp32 accumulators per lane, which
+//   leaves room for two waves per SIMD);
 // * K is walked in steps of BK = 64 through a ring of LDS stages (two by
 //   default): the tiles of the next step are copied from global memory
 //   straight into LDS (buffer_load_dwordx4 ... lds, no staging registers)
