@@ -110,7 +110,9 @@ enum {
  *                 (LMX_ERR_ALIGN otherwise; any two 16-byte aligned buffers do).
  *   target        [B] int64, 8-byte aligned.
  *   B             rows, >= 0 (B = 0 writes loss = NaN for mean, 0 for sum).
- *   V             vocabulary size, 1 <= V < 2^30.
+ *   V             vocabulary size, 1 <= V < 2^30, and one row of `dtype` must
+ *                 stay under 2^31 - 64 bytes (fp32: V < 536870896); the kernels
+ *                 address a row with 32-bit byte offsets (LMX_ERR_SIZE otherwise).
  *   loss          one fp32 on the device (required).
  *   n_valid       one int64 on the device: N; may be NULL.
  *   bad_target    one int32 on the device, set to 1 if a valid target lies
@@ -138,6 +140,9 @@ LMX_API size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype);
  * tokens of the whole call, not of each chunk.
  *
  *   inputs        [BT, D] bf16, row-major, 16-byte aligned; D % 8 == 0.
+ *   Size limits (LMX_ERR_SIZE beyond them; the GEMMs address 256-row panels
+ *   with 32-bit byte offsets): V <= 4194048, D <= 2097088, and at most
+ *   4194240 rows per chunk.
  *   weight        [V, D]  bf16, row-major, 16-byte aligned.
  *   target        [BT] int64.
  *   dtype         LMX_BF16 (the only one implemented; others give
@@ -177,7 +182,8 @@ LMX_API int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size);
  * the equivalent of gather(log_softmax(logits, -1), -1, index), i.e. per row
  * out_i = x[i, index_i] - lse_i, computed with fp32 accumulation.
  *
- *   logits      [B, V] of `dtype`, row-major, element-aligned; 1 <= V < 2^30.
+ *   logits      [B, V] of `dtype`, row-major, element-aligned; V as for
+ *               ce_fwd_bwd.
  *   index       [B] int64 in [0, V), 8-byte aligned.
  *   out         [B] fp32 output, 4-byte aligned, not overlapping the inputs.
  *   bad_index   one int32 on the device, set to 1 if an index lies outside
@@ -198,7 +204,8 @@ LMX_API int selective_log_softmax(const void* logits, const int64_t* index, int6
  * a value no target takes, e.g. -100, to reproduce it exactly); a valid target
  * outside [0, V) sets *bad_target = 1 and gets 0.
  *
- *   logits      [B, V] of `dtype`, row-major, element-aligned; 1 <= V < 2^30.
+ *   logits      [B, V] of `dtype`, row-major, element-aligned; V as for
+ *               ce_fwd_bwd.
  *   target      [B] int64, 8-byte aligned.
  *   loss_rows   [B] fp32 output, 4-byte aligned, not overlapping the inputs.
  *   n_valid, bad_target as for ce_fwd_bwd (may be NULL).
@@ -219,7 +226,8 @@ LMX_API int ce_loss_rows(const void* logits, const int64_t* target, int64_t B, i
  * call is a single read of the logits and a single write of the gradient.
  * Ignored rows, and rows whose target lies outside [0, V), get zero rows.
  *
- *   logits      [B, V] of `dtype`, row-major, element-aligned; 1 <= V < 2^30.
+ *   logits      [B, V] of `dtype`, row-major, element-aligned; V as for
+ *               ce_fwd_bwd.
  *   target      [B] int64, 8-byte aligned.
  *   loss_rows   [B] fp32: ce_loss_rows of the same logits and targets.
  *   g           [B] fp32 upstream gradient per row.

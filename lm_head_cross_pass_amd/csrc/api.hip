@@ -17,6 +17,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// One logits row must fit a 32-bit byte offset (row buffer resources and the
+// kernels' per-row offsets are 32-bit), besides V < 2^30.
+bool row_fits(int64_t V, int dtype) {
+  const int64_t eb = dtype == LMX_BF16 ? 2 : 4;
+  return V > 0 && V < (int64_t{1} << 30) && V * eb <= INT32_MAX - 64;
+}
+
+// Linear-CE limits from the GEMM's 32-bit buffer offsets over 256-row panels
+// (256 rows of the padded vocabulary, of D fp32 values, of the chunk rows).
+constexpr int64_t kLinMaxV = 4194048, kLinMaxD = 2097088, kLinMaxChunk = 4194240;
+
 bool mul_fits(int64_t a, int64_t b, int64_t c) {
   if (a < 0 || b < 0 || c < 0) return false;
   if (a == 0 || b == 0 || c == 0) return true;
@@ -56,7 +67,7 @@ const char* lmx_status_string(int status) {
 }
 
 size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype) {
-  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30) || (dtype != LMX_F32 && dtype != LMX_BF16)) return 0;
+  if (B < 0 || (dtype != LMX_F32 && dtype != LMX_BF16) || !row_fits(V, dtype)) return 0;
   return lmx::ce_workspace_layout(B).total;
 }
 
@@ -66,7 +77,7 @@ int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int
                void* workspace, size_t workspace_bytes, void* stream) {
   if (loss == nullptr || workspace == nullptr) return LMX_ERR_NULL;
   if (B > 0 && (logits == nullptr || target == nullptr)) return LMX_ERR_NULL;
-  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30)) return LMX_ERR_SIZE;
+  if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
   if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
   if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
   const int eb = dtype == LMX_BF16 ? 2 : 4;
@@ -111,7 +122,7 @@ static int rows_forward(const void* logits, const int64_t* target, int64_t B, in
                         void* stream) {
   if (workspace == nullptr) return LMX_ERR_NULL;
   if (B > 0 && (logits == nullptr || target == nullptr || out == nullptr)) return LMX_ERR_NULL;
-  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30)) return LMX_ERR_SIZE;
+  if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
   if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
   const int eb = dtype == LMX_BF16 ? 2 : 4;
   if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
@@ -167,7 +178,7 @@ int ce_loss_rows_vjp(const void* logits, const int64_t* target, const float* los
   if (B > 0 && (logits == nullptr || target == nullptr || loss_rows == nullptr ||
                 g == nullptr || grad_logits == nullptr))
     return LMX_ERR_NULL;
-  if (B < 0 || V <= 0 || V >= (int64_t{1} << 30)) return LMX_ERR_SIZE;
+  if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
   if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
   const int eb = dtype == LMX_BF16 ? 2 : 4;
   if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
@@ -205,7 +216,9 @@ size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
   if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0) return 0;
   if (dtype != LMX_BF16) return 0;
   if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return 0;
+  if (V > kLinMaxV || D > kLinMaxD) return 0;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+  if (c > kLinMaxChunk) return 0;
   return lmx::linear_ce_workspace_layout(BT, D, V, c, accum).total;
 }
 
@@ -218,7 +231,7 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
     return LMX_ERR_NULL;
   if (BT > 0 && (inputs == nullptr || target == nullptr || grad_inputs == nullptr))
     return LMX_ERR_NULL;
-  if (BT < 0 || D <= 0 || V <= 0) return LMX_ERR_SIZE;
+  if (BT < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD) return LMX_ERR_SIZE;
   if (chunk_size < 0) return LMX_ERR_CHUNK;
   if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
   if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
@@ -239,6 +252,7 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
       overlaps(grad_weight, wb, target, BT * 8))
     return LMX_ERR_ALIAS;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+  if (c > kLinMaxChunk) return LMX_ERR_SIZE;
   const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
   lmx::LinearCeParams p;

@@ -334,6 +334,9 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
     const int64_t per_chunk = w.ldv * w.ldc * 2;
     int64_t gsz = (int64_t{1} << 30) / per_chunk;
     if (gsz > nchunks) gsz = nchunks;
+    // the GEMM addresses 256 rows of G^T / X^T with 32-bit byte offsets
+    const int64_t gmax = ((int64_t{1} << 31) - 1) / (256 * 2 * w.ldc);
+    if (gsz > gmax) gsz = gmax;
     if (gsz > 1) w.dw_group = gsz;
   }
   w.ldk = w.dw_group * w.ldc;

@@ -71,10 +71,14 @@ def test_workspace_sizes():
     assert _lib.ce_workspace_bytes(4, 0, F32) == 0
     assert _lib.ce_workspace_bytes(4, 10, 7) == 0
     assert _lib.ce_workspace_bytes(4, 1 << 30, BF16) == 0
+    assert _lib.ce_workspace_bytes(4, (1 << 29) - 8, F32) == 0
+    assert _lib.ce_workspace_bytes(4, (1 << 29) - 8, BF16) > 0
     assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 0) > 0
     assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, F32, 1024, 0) == 0
     assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, -1, 0) == 0
     assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 5) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 4194048 + 1, BF16, 1024, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 2097088 + 8, 1000, BF16, 1024, 0) == 0
 
 
 def test_chunk_rows():
@@ -102,6 +106,7 @@ def _ce(**kw):
     (dict(B=-1), _lib.LMX_ERR_SIZE),
     (dict(V=0), _lib.LMX_ERR_SIZE),
     (dict(V=1 << 30), _lib.LMX_ERR_SIZE),
+    (dict(V=(1 << 29) - 8), _lib.LMX_ERR_SIZE),          # fp32 row past 2^31 - 64 bytes
     (dict(B=1 << 62), _lib.LMX_ERR_SIZE),
     (dict(dtype=2), _lib.LMX_ERR_ENUM),
     (dict(red=2), _lib.LMX_ERR_ENUM),
@@ -135,6 +140,9 @@ def _lin(**kw):
     (dict(BT=-1), _lib.LMX_ERR_SIZE),
     (dict(D=0), _lib.LMX_ERR_SIZE),
     (dict(V=0), _lib.LMX_ERR_SIZE),
+    (dict(V=4194048 + 1), _lib.LMX_ERR_SIZE),           # 32-bit offsets of 256-row panels
+    (dict(D=2097088 + 8), _lib.LMX_ERR_SIZE),
+    (dict(BT=5 << 20, chunk=4194240 + 64), _lib.LMX_ERR_SIZE),  # chunk > 4194240 rows
     (dict(chunk=-1), _lib.LMX_ERR_CHUNK),
     (dict(dtype=F32), _lib.LMX_ERR_UNSUPPORTED),
     (dict(dtype=3), _lib.LMX_ERR_ENUM),
