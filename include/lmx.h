@@ -12,6 +12,14 @@
  *                  materializing the full logits (page entries
  *                  "chunked_linear_loss" and "chunked_linear_cross_entropy").
  *
+ * the building blocks of the generic chunked linear loss, whose per-chunk loss
+ * and logits gradient come from the caller (page entries "chunked_linear_loss"
+ * and "autograd_loss_and_logits_grad"):
+ *
+ *   linear_loss_logits -- the logits of one row chunk, inputs_c @ weight.T;
+ *   linear_loss_grads  -- given the chunk's logits gradient, its grad_inputs
+ *                  rows and the chunk's share of grad_weight;
+ *
  * and three per-row operations on materialized logits:
  *
  *   selective_log_softmax -- log_softmax(x_i)[index_i] per row (greyhound
@@ -170,6 +178,61 @@ LMX_API int linear_ce(const void* inputs, const void* weight, const int64_t* tar
 /* Workspace bytes linear_ce needs (0 for invalid arguments). */
 LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
                                  int64_t chunk_size, int accum);
+
+/*
+ * linear_loss_logits -- logits of one row chunk for the generic chunked loss.
+ *
+ * Greyhound functional API page, entry "chunked_linear_loss": inputs @ weight.T
+ * evaluated in row chunks; this is one chunk, in bf16 with fp32 accumulation
+ * (the page's bf16 matmuls), rounded to nearest even.
+ *
+ *   inputs_c    [rows, D] bf16, 16-byte aligned, D % 8 == 0.
+ *   weight      [V, D] bf16, 16-byte aligned.
+ *   logits      [rows, ld_logits] bf16 output (ld_logits >= V; columns >= V
+ *               are not written), not overlapping the inputs.
+ * Limits as for linear_ce (LMX_ERR_SIZE); dtype must be LMX_BF16. No workspace.
+ */
+LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows,
+                               int64_t D, int64_t V, int dtype, void* logits,
+                               int64_t ld_logits, void* stream);
+
+/*
+ * linear_loss_grads -- gradients of one chunk of the generic chunked loss.
+ *
+ * Greyhound functional API page, entry "chunked_linear_loss": with the chunk's
+ * logits gradient G_c (returned by the caller's loss-and-gradient function),
+ *   grad_inputs[chunk rows] = G_c @ weight,
+ *   grad_weight            (+)= G_c^T @ inputs_c,
+ * accumulated over the chunks in fp32 (LMX_ACC_F32: a workspace accumulator,
+ * rounded to bf16 once, by the last chunk's call) or in grad_weight itself
+ * (LMX_ACC_WEIGHT: rounded after every chunk), the page's
+ * grad_weight_accum_dtype.
+ *
+ * One pass over BT rows is nchunks = ceil(BT / c) calls, c =
+ * linear_ce_chunk_rows(BT, V, chunk_size), with chunk_index 0, 1, ..., in
+ * order, on one stream, sharing one workspace of
+ * linear_loss_workspace_bytes(BT, D, V, dtype, chunk_size, accum) bytes that
+ * must not be touched in between (chunk 0 stores weight.T there for the later
+ * chunks). grad_weight is complete after the call for the last chunk.
+ *
+ *   inputs_c      [rows, D] bf16 rows of this chunk; rows must be the chunk's
+ *                 size (c, or what is left of BT for the last one).
+ *   grad_logits   [rows, ld_grad] bf16, 16-byte aligned; ld_grad >= V and
+ *                 V % 8 == 0 and ld_grad % 8 == 0 (LMX_ERR_ALIGN otherwise).
+ *   grad_inputs_c [rows, D] bf16 output for this chunk's rows.
+ *   grad_weight   [V, D] bf16 output / accumulator.
+ * Outputs must not overlap the inputs (LMX_ERR_ALIAS); a chunk_index outside
+ * [0, nchunks) is LMX_ERR_CHUNK.
+ */
+LMX_API int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad_logits,
+                              int64_t ld_grad, int64_t rows, int64_t BT, int64_t D, int64_t V,
+                              int dtype, int64_t chunk_size, int accum, int64_t chunk_index,
+                              void* grad_inputs_c, void* grad_weight, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Workspace bytes linear_loss_grads needs for one pass (0 for invalid arguments). */
+LMX_API size_t linear_loss_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
+                                           int64_t chunk_size, int accum);
 
 /* Rows per chunk that linear_ce uses for this chunk_size argument (resolves 0). */
 LMX_API int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size);

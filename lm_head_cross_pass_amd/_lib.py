@@ -44,6 +44,10 @@ _SIGNATURES = {
     "selective_log_softmax": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "ce_loss_rows": (_i32, [_vp, _vp, _i64, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ce_loss_rows_vjp": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp]),
+    "linear_loss_logits": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp]),
+    "linear_loss_grads": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i32, _i64, _i32,
+                                 _i64, _vp, _vp, _vp, _sz, _vp]),
+    "linear_loss_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32]),
 }
 
 _lib = None
@@ -138,3 +142,19 @@ def ce_loss_rows_vjp(logits, target, loss_rows, g, grad_logits, B, V, dtype, ign
                      stream) -> int:
     return load().ce_loss_rows_vjp(logits, target, loss_rows, g, grad_logits, B, V, dtype,
                                    ignore_index, stream)
+
+
+def linear_loss_logits(inputs_c, weight, rows, D, V, dtype, logits, ld_logits, stream) -> int:
+    return load().linear_loss_logits(inputs_c, weight, rows, D, V, dtype, logits, ld_logits, stream)
+
+
+def linear_loss_grads(inputs_c, weight, grad_logits, ld_grad, rows, BT, D, V, dtype, chunk_size,
+                      accum, chunk_index, grad_inputs_c, grad_weight, workspace, workspace_bytes,
+                      stream) -> int:
+    return load().linear_loss_grads(inputs_c, weight, grad_logits, ld_grad, rows, BT, D, V, dtype,
+                                    chunk_size, accum, chunk_index, grad_inputs_c, grad_weight,
+                                    workspace, workspace_bytes, stream)
+
+
+def linear_loss_workspace_bytes(BT, D, V, dtype, chunk_size, accum) -> int:
+    return load().linear_loss_workspace_bytes(BT, D, V, dtype, chunk_size, accum)

@@ -206,6 +206,91 @@ int ce_loss_rows_vjp(const void* logits, const int64_t* target, const float* los
   return lmx::ce_vjp_enqueue(p, dtype, static_cast<hipStream_t>(stream));
 }
 
+size_t linear_loss_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
+                                   int64_t chunk_size, int accum) {
+  if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0) return 0;
+  if (dtype != LMX_BF16) return 0;
+  if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return 0;
+  if (V > kLinMaxV || D > kLinMaxD) return 0;
+  const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+  if (c > kLinMaxChunk) return 0;
+  return lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true).total;
+}
+
+int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, int64_t D,
+                       int64_t V, int dtype, void* logits, int64_t ld_logits, void* stream) {
+  if (weight == nullptr || (rows > 0 && (inputs_c == nullptr || logits == nullptr)))
+    return LMX_ERR_NULL;
+  if (rows < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || rows > kLinMaxChunk ||
+      ld_logits < V)
+    return LMX_ERR_SIZE;
+  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (dtype != LMX_BF16) return LMX_ERR_UNSUPPORTED;
+  if (D % 8 != 0 || reinterpret_cast<uintptr_t>(inputs_c) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(weight) % 16 != 0 || reinterpret_cast<uintptr_t>(logits) % 2 != 0)
+    return LMX_ERR_ALIGN;
+  const size_t lb = static_cast<size_t>(rows > 0 ? rows - 1 : 0) * ld_logits * 2 + V * 2;
+  if (rows > 0 && (overlaps(logits, lb, inputs_c, static_cast<size_t>(rows) * D * 2) ||
+                   overlaps(logits, lb, weight, static_cast<size_t>(V) * D * 2)))
+    return LMX_ERR_ALIAS;
+  return lmx::linear_loss_logits_enqueue(static_cast<const uint16_t*>(inputs_c),
+                                         static_cast<const uint16_t*>(weight),
+                                         static_cast<int>(rows), static_cast<int>(D),
+                                         static_cast<int>(V), static_cast<uint16_t*>(logits),
+                                         ld_logits, static_cast<hipStream_t>(stream));
+}
+
+int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad_logits,
+                      int64_t ld_grad, int64_t rows, int64_t BT, int64_t D, int64_t V, int dtype,
+                      int64_t chunk_size, int accum, int64_t chunk_index, void* grad_inputs_c,
+                      void* grad_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  if (weight == nullptr || grad_weight == nullptr || workspace == nullptr) return LMX_ERR_NULL;
+  if (rows > 0 && (inputs_c == nullptr || grad_logits == nullptr || grad_inputs_c == nullptr))
+    return LMX_ERR_NULL;
+  if (BT <= 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || ld_grad < V)
+    return LMX_ERR_SIZE;
+  if (chunk_size < 0) return LMX_ERR_CHUNK;
+  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return LMX_ERR_ENUM;
+  if (dtype != LMX_BF16) return LMX_ERR_UNSUPPORTED;
+  const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
+  if (c > kLinMaxChunk) return LMX_ERR_SIZE;
+  const int64_t nchunks = (BT + c - 1) / c;
+  if (chunk_index < 0 || chunk_index >= nchunks) return LMX_ERR_CHUNK;
+  const int64_t expect = BT - chunk_index * c < c ? BT - chunk_index * c : c;
+  if (rows != expect) return LMX_ERR_SIZE;
+  if (D % 8 != 0 || V % 8 != 0 || ld_grad % 8 != 0) return LMX_ERR_ALIGN;
+  for (const void* q : {inputs_c, weight, grad_logits, static_cast<const void*>(grad_inputs_c),
+                        static_cast<const void*>(grad_weight)}) {
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return LMX_ERR_ALIGN;
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return LMX_ERR_WORKSPACE;
+  const size_t xb = static_cast<size_t>(rows) * D * 2, wb = static_cast<size_t>(V) * D * 2;
+  const size_t gb = static_cast<size_t>(rows) * ld_grad * 2;
+  if (overlaps(grad_inputs_c, xb, inputs_c, xb) || overlaps(grad_inputs_c, xb, weight, wb) ||
+      overlaps(grad_inputs_c, xb, grad_logits, gb) || overlaps(grad_weight, wb, inputs_c, xb) ||
+      overlaps(grad_weight, wb, weight, wb) || overlaps(grad_weight, wb, grad_logits, gb) ||
+      overlaps(grad_inputs_c, xb, grad_weight, wb))
+    return LMX_ERR_ALIAS;
+  const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true);
+  if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
+  lmx::LinearLossChunk p{};
+  p.xc = static_cast<const uint16_t*>(inputs_c);
+  p.w = static_cast<const uint16_t*>(weight);
+  p.g = static_cast<const uint16_t*>(grad_logits);
+  p.ld_g = ld_grad;
+  p.rows = static_cast<int>(rows);
+  p.BT = BT;
+  p.D = D;
+  p.V = V;
+  p.chunk = c;
+  p.accum = accum;
+  p.index = chunk_index;
+  p.grad_xc = static_cast<uint16_t*>(grad_inputs_c);
+  p.grad_w = static_cast<uint16_t*>(grad_weight);
+  return lmx::linear_loss_grads_enqueue(p, workspace, static_cast<hipStream_t>(stream));
+}
+
 int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size) {
   if (BT < 0 || V <= 0 || chunk_size < 0) return 0;
   return lmx::linear_ce_resolve_chunk(BT, V, chunk_size);

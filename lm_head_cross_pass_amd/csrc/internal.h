@@ -85,10 +85,30 @@ struct LinearCeWorkspace {
   int64_t ldk;              // row stride of G^T and X_c^T: dw_group * ldc
   size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, dxp_off, dw_off, total;
 };
+// generic = true: the layout of the generic chunked loss (no chunk logits
+// buffer: the caller holds them; one grad_weight product per chunk).
 LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, int64_t chunk,
-                                             int accum);
+                                             int accum, bool generic = false);
 int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size);
 int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream);
+
+// Generic chunked linear loss (the caller's loss and logits gradient per chunk):
+// logits of one chunk, then its gradients.
+int linear_loss_logits_enqueue(const uint16_t* xc, const uint16_t* w, int rows, int D, int V,
+                               uint16_t* logits, int64_t ld_logits, hipStream_t stream);
+struct LinearLossChunk {
+  const uint16_t* xc;       // [rows, D] bf16
+  const uint16_t* w;        // [V, D] bf16
+  const uint16_t* g;        // [rows, ld_g] bf16: d(loss)/d(logits) of the chunk
+  int64_t ld_g;
+  int rows;
+  int64_t BT, D, V, chunk;  // chunk: rows per chunk of the whole pass (resolved)
+  int accum;
+  int64_t index;            // chunk number within the pass
+  uint16_t* grad_xc;        // [rows, D] bf16
+  uint16_t* grad_w;         // [V, D] bf16
+};
+int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws, hipStream_t stream);
 
 int copy_enqueue(const void* src, void* dst, size_t bytes, hipStream_t stream);
 

@@ -304,6 +304,37 @@ int dx_ksplit(int64_t C, int64_t D, int64_t ldv) {
   return static_cast<int>(s);
 }
 
+// grad_inputs rows of one chunk: G [rows, lda_g] times W, with W^T [D, ldv] as
+// the K-contiguous operand over K = k_len vocabulary columns; split-K partials
+// in dxp when the layout chose splits.
+int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_t* wt,
+                      int64_t ldv, int rows, int D, int64_t chunk, int ksplit, float* dxp,
+                      uint16_t* gx, int64_t ldx, hipStream_t stream) {
+  const int tile = pick_tile(chunk, D, 2);   // the tile the workspace was sized for
+  GemmShape gs = make_shape(g, lda_g, wt, ldv, rows, D, D, k_len, ksplit, tile);
+  EpiBf16 e{gx, ldx, dxp, D};
+  int st = launch_gemm<1>(gs, tile, e, stream);
+  if (st != LMX_OK) return st;
+  if (gs.ksplit > 1) {
+    const int64_t total = static_cast<int64_t>(rows) * D / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                       dim3(256), 0, stream, dxp, gs.ksplit, rows, D, static_cast<int64_t>(D),
+                       gx, ldx);
+    if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
+  }
+  return LMX_OK;
+}
+
+// grad_weight product G^T X over K columns of G^T [V, ldk] and X^T [D, ldk],
+// stored or accumulated according to `mode`.
+int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int K, int V, int D,
+                        float* dw, uint16_t* gw, int64_t ldw, int mode, hipStream_t stream) {
+  const int tile = pick_tile(V, D);
+  GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
+  EpiDw e{dw, gw, ldw, mode};
+  return launch_gemm<1>(gs, tile, e, stream);
+}
+
 }  // namespace
 
 int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size) {
@@ -319,7 +350,7 @@ int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size) {
 }
 
 LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, int64_t chunk,
-                                             int accum) {
+                                             int accum, bool generic) {
   LinearCeWorkspace w{};
   const int64_t C = chunk > 0 ? chunk : 1;
   w.ldv = round_up64(V, kLdvAlign);
@@ -330,7 +361,7 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   // (K = group ldc): as many chunks as G^T of 1 GiB holds, so the fp32
   // accumulator is read and written once per group instead of once per chunk
   w.dw_group = 1;
-  if (accum == LMX_ACC_F32 && nchunks > 1) {
+  if (accum == LMX_ACC_F32 && nchunks > 1 && !generic) {
     const int64_t per_chunk = w.ldv * w.ldc * 2;
     int64_t gsz = (int64_t{1} << 30) / per_chunk;
     if (gsz > nchunks) gsz = nchunks;
@@ -348,7 +379,7 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   };
   w.n_valid_off = take(8);
   w.row_loss_off = take(static_cast<size_t>(BT) * 4);
-  w.z_off = take(static_cast<size_t>(C) * w.ldv * 2);
+  w.z_off = take(generic ? 0 : static_cast<size_t>(C) * w.ldv * 2);
   w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldk * 2);
   w.xt_off = take(static_cast<size_t>(D) * w.ldk * 2);
   w.wt_off = take(static_cast<size_t>(D) * w.ldv * 2);
@@ -422,21 +453,9 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
     st = transpose_pad(z, ldv, rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
     // 5. grad_inputs rows
-    {
-      const int tile = pick_tile(p.chunk, D, 2);   // the tile the workspace was sized for
-      GemmShape g = make_shape(z, ldv, wt, ldv, rows, D, D, static_cast<int>(ldv),
-                               static_cast<int>(wl.ksplit), tile);
-      EpiBf16 e{p.grad_x + r0 * p.D, p.D, dxp, p.D};
-      st = launch_gemm<1>(g, tile, e, stream);
-      if (st != LMX_OK) return st;
-      if (g.ksplit > 1) {
-        const int64_t total = static_cast<int64_t>(rows) * D / 4;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
-                           dim3(256), 0, stream, dxp, g.ksplit, rows, D, p.D, p.grad_x + r0 * p.D,
-                           p.D);
-        if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
-      }
-    }
+    st = chunk_grad_inputs(z, ldv, static_cast<int>(ldv), wt, ldv, rows, D, p.chunk,
+                           static_cast<int>(wl.ksplit), dxp, p.grad_x + r0 * p.D, p.D, stream);
+    if (st != LMX_OK) return st;
     // 6. grad_weight, once per group of chunks
     if (slot == grp - 1 || c == nchunks - 1) {
       const int64_t gi = c / grp, ngroups = (nchunks + grp - 1) / grp;
@@ -447,15 +466,55 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       } else {
         mode = first ? kDwStoreBf16 : kDwAddBf16;
       }
-      const int tile = pick_tile(V, D);
-      GemmShape g = make_shape(gt, ldk, xt, ldk, V, D, D, static_cast<int>((slot + 1) * ldc), 1,
-                               tile);
-      EpiDw e{dw, p.grad_w, p.D, mode};
-      st = launch_gemm<1>(g, tile, e, stream);
+      st = grad_weight_product(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw, p.grad_w,
+                               p.D, mode, stream);
       if (st != LMX_OK) return st;
     }
   }
   return finish_enqueue(row_loss, p.BT, n_ws, p.reduction, p.loss, stream);
+}
+
+int linear_loss_logits_enqueue(const uint16_t* xc, const uint16_t* w, int rows, int D, int V,
+                               uint16_t* logits, int64_t ld_logits, hipStream_t stream) {
+  if (rows == 0) return LMX_OK;
+  const int tile = pick_tile(rows, V);
+  GemmShape g = make_shape(xc, D, w, D, rows, V, V, D, 1, tile);
+  EpiBf16 e{logits, ld_logits, nullptr, 0};
+  return launch_gemm<1>(g, tile, e, stream);
+}
+
+int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws_base, hipStream_t stream) {
+  const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum, true);
+  char* ws = static_cast<char*>(ws_base);
+  uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
+  float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
+  float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
+  const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
+  const int64_t ldv = wl.ldv, ldc = wl.ldc;
+  const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
+  int st;
+  if (p.index == 0) {   // W^T for every chunk of the pass
+    st = transpose_pad(p.w, p.D, V, D, wt, ldv, static_cast<int>(ldv), stream);
+    if (st != LMX_OK) return st;
+  }
+  st = transpose_pad(p.xc, p.D, p.rows, D, xt, ldc, static_cast<int>(ldc), stream);
+  if (st != LMX_OK) return st;
+  st = transpose_pad(p.g, p.ld_g, p.rows, V, gt, ldc, static_cast<int>(ldc), stream);
+  if (st != LMX_OK) return st;
+  st = chunk_grad_inputs(p.g, p.ld_g, V, wt, ldv, p.rows, D, p.chunk,
+                         static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, stream);
+  if (st != LMX_OK) return st;
+  const bool first = p.index == 0, last = p.index == nchunks - 1;
+  int mode;
+  if (p.accum == LMX_ACC_F32) {
+    mode = nchunks == 1 ? kDwStoreBf16 : first ? kDwStoreF32 : last ? kDwAddF32ToBf16 : kDwAddF32;
+  } else {
+    mode = first ? kDwStoreBf16 : kDwAddBf16;
+  }
+  return grad_weight_product(gt, xt, ldc, static_cast<int>(ldc), V, D, dw, p.grad_w, p.D, mode,
+                             stream);
 }
 
 }  // namespace lmx

@@ -10,6 +10,12 @@ computation runs in the library's kernels. The functions:
 * ``linear_cross_entropy`` -- chunked ``inputs @ weight.T`` cross-entropy with
   gradients for inputs and weight (page entries ``chunked_linear_loss`` and
   ``chunked_linear_cross_entropy``; ``chunk_size`` as in the former);
+* ``chunked_linear_loss`` with ``autograd_loss_and_logits_grad`` -- the
+  generic chunked linear loss: the library computes each chunk's logits and,
+  from the caller's logits gradient, the chunk's grad_inputs rows and its
+  share of grad_weight (page entries ``chunked_linear_loss`` and
+  ``autograd_loss_and_logits_grad``); ``cross_entropy_loss_and_grad`` is the
+  library's cross-entropy in that loss-and-gradient form;
 * ``selective_log_softmax`` -- one log-probability per row (page entry
   ``selective_log_softmax``);
 * ``cross_entropy_per_row`` -- the unreduced per-row cross-entropy whose
@@ -272,3 +278,114 @@ def cross_entropy_per_row(logits: torch.Tensor, target: torch.Tensor,
     """Unreduced cross-entropy ``logsumexp(x_i) - x_i[t_i]`` per row (fp32 [B], 0 where
     ignored); its backward is one ``ce_loss_rows_vjp`` pass over the logits."""
     return _CrossEntropyPerRow.apply(logits, target, ignore_index)
+
+
+def autograd_loss_and_logits_grad(loss_fn):
+    """Adapts a scalar loss ``loss_fn(logits_chunk, *args, **kwargs)`` to return
+    ``(loss, grad_logits)`` by running autograd on the logits chunk (page entry
+    ``autograd_loss_and_logits_grad``)."""
+    def loss_and_grad(logits_chunk, *args, **kwargs):
+        x = logits_chunk.detach().requires_grad_(True)
+        with torch.enable_grad():
+            loss = loss_fn(x, *args, **kwargs)
+            (g,) = torch.autograd.grad(loss, x)
+        return loss.detach(), g
+    return loss_and_grad
+
+
+def cross_entropy_loss_and_grad(logits_chunk: torch.Tensor, target: torch.Tensor,
+                                ignore_index: int = -100, z_loss_multiplier: float = 0.0):
+    """The library's cross-entropy (sum over the chunk's valid rows) as a
+    loss-and-gradient function for ``chunked_linear_loss``; the gradient is
+    written over the logits chunk, which ``chunked_linear_loss`` allows."""
+    loss, _, _, _ = ce_fwd_bwd(logits_chunk, target, ignore_index, "sum", z_loss_multiplier,
+                               in_place=True)
+    return loss, logits_chunk
+
+
+def _slice_rows(v, BT: int, r0: int, r1: int):
+    if isinstance(v, torch.Tensor) and v.dim() > 0 and v.shape[0] == BT:
+        return v[r0:r1]
+    return v
+
+
+def chunked_linear_loss_fwd(inputs: torch.Tensor, weight: torch.Tensor, loss_and_grad_fn,
+                            loss_args=(), loss_kwargs=None, chunk_size: Optional[int] = None,
+                            grad_weight_accum_dtype: str = "fp32", workspace=None):
+    """One pass: (sum of the chunk losses, grad_inputs, grad_weight) for an upstream
+    gradient of 1. The logits chunk handed to ``loss_and_grad_fn`` is a fresh
+    [rows, V] bf16 tensor, which the function may overwrite with its gradient."""
+    loss_kwargs = loss_kwargs or {}
+    for t, n in ((inputs, "inputs"), (weight, "weight")):
+        _require_device(t, n)
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 2-D tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bfloat16 (the matmuls run in bf16)")
+    BT, D = inputs.shape
+    V, D2 = weight.shape
+    if D2 != D:
+        raise ValueError("inputs [BT, D] and weight [V, D] disagree on D")
+    if V % 8 != 0:
+        raise ValueError("the generic chunked loss needs V % 8 == 0 (16-byte gradient rows)")
+    if grad_weight_accum_dtype not in _ACCUMS:
+        raise ValueError("grad_weight_accum_dtype must be 'fp32' or 'weight'")
+    dev = inputs.device
+    cs = 0 if chunk_size is None else int(chunk_size)
+    acc = _ACCUMS[grad_weight_accum_dtype]
+    gx = torch.empty_like(inputs)
+    gw = torch.empty_like(weight)
+    total = torch.zeros((), dtype=torch.float32, device=dev)
+    if BT == 0:
+        gw.zero_()
+        return total, gx, gw
+    C = _lib.linear_ce_chunk_rows(BT, V, cs)
+    nbytes = _lib.linear_loss_workspace_bytes(BT, D, V, _lib.LMX_BF16, cs, acc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, dev)
+    stream = _stream_handle(dev)
+    with torch.cuda.device(dev):
+        for ci, r0 in enumerate(range(0, BT, C)):
+            r1 = min(BT, r0 + C)
+            rows = r1 - r0
+            logits = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
+            _lib.check("linear_loss_logits", _lib.linear_loss_logits(
+                inputs[r0:r1].data_ptr(), weight.data_ptr(), rows, D, V, _lib.LMX_BF16,
+                logits.data_ptr(), V, stream))
+            args = [_slice_rows(a, BT, r0, r1) for a in loss_args]
+            kwargs = {k: _slice_rows(v, BT, r0, r1) for k, v in loss_kwargs.items()}
+            loss_c, g = loss_and_grad_fn(logits, *args, **kwargs)
+            if g.shape != (rows, V):
+                raise ValueError("loss_and_grad_fn must return a gradient shaped like the logits")
+            g = g.to(torch.bfloat16).contiguous()
+            total += loss_c.detach().to(torch.float32)
+            _lib.check("linear_loss_grads", _lib.linear_loss_grads(
+                inputs[r0:r1].data_ptr(), weight.data_ptr(), g.data_ptr(), V, rows, BT, D, V,
+                _lib.LMX_BF16, cs, acc, ci, gx[r0:r1].data_ptr(), gw.data_ptr(),
+                workspace.data_ptr(), workspace.numel(), stream))
+    return total, gx, gw
+
+
+class _ChunkedLinearLoss(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, inputs, weight, fn, args, kwargs, chunk_size, accum):
+        loss, gx, gw = chunked_linear_loss_fwd(inputs.detach(), weight.detach(), fn, args, kwargs,
+                                               chunk_size, accum)
+        ctx.save_for_backward(gx, gw)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        gx, gw = ctx.saved_tensors
+        g = grad_out.to(gx.dtype)
+        return gx * g, gw * g, None, None, None, None, None
+
+
+def chunked_linear_loss(inputs: torch.Tensor, weight: torch.Tensor, loss_and_grad_fn,
+                        *loss_args, chunk_size: Optional[int] = None,
+                        grad_weight_accum_dtype: str = "fp32", **loss_kwargs) -> torch.Tensor:
+    """Sum over row chunks of ``loss_and_grad_fn(inputs_c @ weight.T, *args_c, **kwargs_c)[0]``,
+    with gradients for inputs and weight accumulated chunk by chunk (tensor
+    arguments whose leading dimension is BT are sliced to the chunk's rows)."""
+    return _ChunkedLinearLoss.apply(inputs, weight, loss_and_grad_fn, loss_args, loss_kwargs,
+                                    chunk_size, grad_weight_accum_dtype)

@@ -15,6 +15,9 @@ Modules:
   the same loss, and the gradients of ``inputs`` and ``weight``, plus the
   chunk-by-chunk weight-dtype accumulation (greyhound functional API page,
   ``chunked_linear_loss`` and ``chunked_linear_cross_entropy``).
+* ``oracle.generic`` -- the generic chunked linear loss (greyhound
+  functional API page, ``chunked_linear_loss``) for losses that are sums over
+  rows, with ``mse_sum`` as the written-out example.
 * ``oracle.rows``      -- per-row operations: ``selective_log_softmax``
   (greyhound functional API page) and the unreduced per-row cross-entropy
   with its vector-Jacobian product (nuvec ``FastOp`` page, ``CrossEntropy`` and
@@ -29,5 +32,6 @@ reductions to library routines).
 from oracle.ce import cross_entropy, cross_entropy_rows, count_valid  # noqa: F401
 from oracle.linear_ce import linear_cross_entropy  # noqa: F401
 from oracle.bf16 import round_to_bf16  # noqa: F401
+from oracle.generic import linear_loss, mse_sum  # noqa: F401
 from oracle.rows import (cross_entropy_per_row, cross_entropy_per_row_vjp,  # noqa: F401
                          selective_log_softmax)

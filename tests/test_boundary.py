@@ -31,7 +31,8 @@ def test_every_declared_function_is_exported():
     assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "linear_ce",
                           "linear_ce_workspace_bytes", "linear_ce_chunk_rows",
                           "lmx_status_string", "lmx_copy", "selective_log_softmax",
-                          "ce_loss_rows", "ce_loss_rows_vjp"}
+                          "ce_loss_rows", "ce_loss_rows_vjp", "linear_loss_logits",
+                          "linear_loss_grads", "linear_loss_workspace_bytes"}
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -225,3 +226,47 @@ def _vjp(**kw):
 ])
 def test_vjp_argument_errors(kw, status):
     assert _vjp(**kw) == status
+
+
+def _grads(**kw):
+    args = dict(x=A, w=A + (1 << 34), g=A + (2 << 34), ldg=1000, rows=16, BT=64, D=64, V=1000,
+                dtype=BF16, chunk=16, acc=0, idx=0, gx=A + (5 << 34), gw=A + (6 << 34),
+                ws=A + (4 << 34), wsb=1 << 40, stream=None)
+    args.update(kw)
+    return _lib.linear_loss_grads(args["x"], args["w"], args["g"], args["ldg"], args["rows"],
+                                  args["BT"], args["D"], args["V"], args["dtype"], args["chunk"],
+                                  args["acc"], args["idx"], args["gx"], args["gw"], args["ws"],
+                                  args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gw=None), _lib.LMX_ERR_NULL),
+    (dict(g=None), _lib.LMX_ERR_NULL),
+    (dict(BT=0), _lib.LMX_ERR_SIZE),
+    (dict(ldg=999), _lib.LMX_ERR_SIZE),
+    (dict(rows=15), _lib.LMX_ERR_SIZE),                   # not the chunk's size
+    (dict(idx=4), _lib.LMX_ERR_CHUNK),                    # 64 / 16 = 4 chunks
+    (dict(idx=-1), _lib.LMX_ERR_CHUNK),
+    (dict(chunk=-2), _lib.LMX_ERR_CHUNK),
+    (dict(dtype=F32), _lib.LMX_ERR_UNSUPPORTED),
+    (dict(acc=3), _lib.LMX_ERR_ENUM),
+    (dict(V=1001, ldg=1001), _lib.LMX_ERR_ALIGN),         # gradient rows must be 16-byte rows
+    (dict(g=A + (2 << 34) + 8), _lib.LMX_ERR_ALIGN),
+    (dict(ws=A + (4 << 34) + 128), _lib.LMX_ERR_WORKSPACE),
+    (dict(wsb=1024), _lib.LMX_ERR_WORKSPACE),
+    (dict(gx=A + (2 << 34) + 64), _lib.LMX_ERR_ALIAS),   # inside the logits gradient
+])
+def test_linear_loss_grads_argument_errors(kw, status):
+    assert _grads(**kw) == status
+
+
+def test_linear_loss_logits_argument_errors():
+    f = _lib.linear_loss_logits
+    assert f(A, None, 16, 64, 1000, BF16, A + (3 << 34), 1000, None) == _lib.LMX_ERR_NULL
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + (3 << 34), 999, None) == _lib.LMX_ERR_SIZE
+    assert f(A, A + (1 << 34), 16, 64, 1000, 7, A + (3 << 34), 1000, None) == _lib.LMX_ERR_ENUM
+    assert f(A, A + (1 << 34), 16, 60, 1000, BF16, A + (3 << 34), 1000, None) == _lib.LMX_ERR_ALIGN
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + 64, 1000, None) == _lib.LMX_ERR_ALIAS
+    assert f(None, A, 0, 64, 1000, BF16, None, 1000, None) == _lib.LMX_OK
+    assert _lib.linear_loss_workspace_bytes(64, 64, 1000, BF16, 16, 0) > 0
+    assert _lib.linear_loss_workspace_bytes(64, 64, 1000, F32, 16, 0) == 0
