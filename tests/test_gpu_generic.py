@@ -1,0 +1,105 @@
+"""GPU parity of the generic chunked linear loss (linear_loss_logits /
+linear_loss_grads through ``chunked_linear_loss``) against the fp64 oracle.
+
+The loss-and-gradient functions are the caller's: a sum-of-squares loss through
+``autograd_loss_and_logits_grad`` (torch autograd on the chunk), torch's
+cross-entropy the same way, and the library's own cross-entropy
+(``cross_entropy_loss_and_grad``). The logits are bf16 (the matmuls' dtype), so
+the bars are those of the bf16 linear path: loss within 5e-3 relative (2e-3 for
+cross-entropy), each gradient within 1e-2 relative Frobenius norm. Y (the
+regression targets) and the other inputs come from the seeded generators.
+"""
+import pytest
+import torch
+import torch.nn.functional as TF
+
+import oracle
+from oracle import generic as ogen
+import workloads
+from lm_head_cross_pass_amd import functional as F
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _rel(got, ref):
+    got = got.double().cpu()
+    n = float(ref.norm())
+    return float((got - ref).norm()) / n if n > 0 else float(got.norm())
+
+
+def _mse(z, y):
+    return TF.mse_loss(z.float(), y, reduction="sum")
+
+
+@pytest.mark.parametrize("BT,D,V,chunk", [(96, 64, 512, 32), (100, 72, 336, 37),
+                                          (257, 128, 4096, 100), (64, 64, 1000, 0)])
+@pytest.mark.parametrize("accum", ("fp32", "weight"))
+def test_sum_of_squares_loss(BT, D, V, chunk, accum):
+    X, W, _ = workloads.small_linear_ce(BT, D, V, seed=BT + V, sigma_w=0.1)
+    Y = workloads.row_upstream(BT * V, seed=V).reshape(BT, V) * 0.5
+    loss, gx, gw = F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV),
+                                             F.autograd_loss_and_logits_grad(_mse), (Y.to(DEV),),
+                                             chunk_size=chunk or None,
+                                             grad_weight_accum_dtype=accum)
+    torch.cuda.synchronize()
+    ref = ogen.linear_loss(X, W, ogen.mse_sum, Y)
+    assert float(loss) == pytest.approx(ref["loss"], rel=5e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+@pytest.mark.parametrize("how", ("library", "torch"))
+def test_cross_entropy_through_the_generic_path(how):
+    BT, D, V = 300, 96, 2048
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=15, seed=9)
+    if how == "library":
+        fn = F.cross_entropy_loss_and_grad
+    else:
+        fn = F.autograd_loss_and_logits_grad(
+            lambda z, tt: TF.cross_entropy(z.float(), tt, ignore_index=-100, reduction="sum"))
+    loss, gx, gw = F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV), fn, (t.to(DEV),),
+                                             chunk_size=64)
+    torch.cuda.synchronize()
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+def test_generic_matches_fused_linear_ce():
+    # the library's CE through the generic path against the fused linear_ce
+    BT, D, V = 512, 128, 4096
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=20, seed=3)
+    Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
+    loss_g, gx_g, gw_g = F.chunked_linear_loss_fwd(Xd, Wd, F.cross_entropy_loss_and_grad, (td,),
+                                                   chunk_size=128)
+    loss_f, gx_f, gw_f, _, _ = F.linear_ce(Xd, Wd, td, -100, "sum", 0.0, 128, "fp32")
+    torch.cuda.synchronize()
+    assert float(loss_g) == pytest.approx(float(loss_f), rel=1e-5)
+    assert _rel(gx_g, gx_f.double().cpu()) <= 1e-2
+    assert _rel(gw_g, gw_f.double().cpu()) <= 1e-2
+
+
+def test_autograd_and_argument_slicing():
+    BT, D, V = 128, 64, 256
+    X, W, _ = workloads.small_linear_ce(BT, D, V, seed=2, sigma_w=0.1)
+    Y = workloads.row_upstream(BT * V, seed=2).reshape(BT, V)
+    scale = 0.5
+    Xd = X.to(DEV).requires_grad_(True)
+    Wd = W.to(DEV).requires_grad_(True)
+    loss = F.chunked_linear_loss(Xd, Wd, F.autograd_loss_and_logits_grad(_mse), Y.to(DEV),
+                                 chunk_size=48)
+    (loss * scale).backward()
+    torch.cuda.synchronize()
+    ref = ogen.linear_loss(X, W, ogen.mse_sum, Y)
+    assert float(loss.detach()) == pytest.approx(ref["loss"], rel=5e-3)
+    assert _rel(Xd.grad, scale * ref["grad_inputs"]) <= 1e-2
+    assert _rel(Wd.grad, scale * ref["grad_weight"]) <= 1e-2
+
+
+def test_vocabulary_must_give_16_byte_gradient_rows():
+    X, W, _ = workloads.small_linear_ce(32, 64, 1001, seed=1)
+    with pytest.raises(ValueError):
+        F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV), F.cross_entropy_loss_and_grad,
+                                  (torch.zeros(32, dtype=torch.int64, device=DEV),))
