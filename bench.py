@@ -18,10 +18,12 @@ roofline against the 8 TB/s HBM peak, and the linear-CE leg under
 dense bf16 MFMA peak), plus its 'weight'-accumulation variant timed on its own.
 ``next_rows`` times the per-row entry points on the CE leg's logits (forward-only
 reduced CE, selective_log_softmax, the unreduced per-row CE and its VJP), each
-in GB/s of its own algorithmic bytes. ``cpu_baseline`` is the fp64 oracle timed
+in GB/s of its own algorithmic bytes; ``linear_ce.generic_chunked_loss`` times the
+generic chunked linear loss with the library's cross-entropy as the caller's loss
+on the linear-CE inputs. ``cpu_baseline`` is the fp64 oracle timed
 on the host on a bounded sample of the same CE workload.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows,generic] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -81,8 +83,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="ce,linear,rows",
-                    help="ce, linear, rows (the per-row entry points; needs ce)")
+    ap.add_argument("--legs", default="ce,linear,rows,generic",
+                    help="ce, linear, rows (per-row entry points; needs ce), generic (the "
+                         "generic chunked linear loss; needs linear)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--weight-steps", type=int, default=3)
     args = ap.parse_args()
@@ -230,6 +233,30 @@ def main() -> int:
             wms = e0.elapsed_time(e1) / args.weight_steps
             lin["weight_accum"] = {"value": round(flops / (wms * 1e-3) / 1e12, 1),
                                    "unit": "TFLOP/s", "ms_per_call": round(wms, 3)}
+        # the generic chunked loss with the library's cross-entropy as the caller's
+        # loss (sum reduction, fp32 accumulation), on the same inputs
+        if "generic" in legs:
+            from lm_head_cross_pass_amd import functional as LF
+            gen_ws = torch.empty(_lib.linear_loss_workspace_bytes(
+                lin_w.BT, lin_w.D, lin_w.V, _lib.LMX_BF16, lin_w.chunk_size, _lib.LMX_ACC_F32),
+                dtype=torch.uint8, device=dev)
+
+            def gen_call():
+                return LF.chunked_linear_loss_fwd(X, Wt, LF.cross_entropy_loss_and_grad, (tl,),
+                                                  chunk_size=lin_w.chunk_size, workspace=gen_ws)
+            gen_call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(3):
+                gen_call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gms = e0.elapsed_time(e1) / 3
+            lin["generic_chunked_loss"] = {"value": round(flops / (gms * 1e-3) / 1e12, 1),
+                                           "unit": "TFLOP/s", "ms_per_call": round(gms, 3),
+                                           "loss": "library cross-entropy, sum"}
+            log(f"generic chunked loss: {gms:.3f} ms")
         line["linear_ce"] = lin
         workload_names.append(lin_w.name)
         line["config"].update({"lin_BT": lin_w.BT, "lin_D": lin_w.D, "lin_V": lin_w.V,
