@@ -22,8 +22,9 @@ Modules:
   (greyhound functional API page) and the unreduced per-row cross-entropy
   with its vector-Jacobian product (nuvec ``FastOp`` page, ``CrossEntropy`` and
   ``CrossEntropyVjp``).
-* ``oracle.bf16``      -- round-to-nearest-even to bfloat16, written from the
-  format's definition; used only by the weight-dtype accumulation emulation.
+* ``oracle.bf16``, ``oracle.fp16`` -- round-to-nearest-even to bfloat16 and to
+  IEEE binary16, written from the formats' definitions; used only by the
+  weight-dtype accumulation emulation.
 
 Every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (finite differences, closed forms, invariants and
@@ -32,6 +33,7 @@ reductions to library routines).
 from oracle.ce import cross_entropy, cross_entropy_rows, count_valid  # noqa: F401
 from oracle.linear_ce import linear_cross_entropy  # noqa: F401
 from oracle.bf16 import round_to_bf16  # noqa: F401
+from oracle.fp16 import round_to_fp16  # noqa: F401
 from oracle.generic import linear_loss, mse_sum  # noqa: F401
 from oracle.rows import (cross_entropy_per_row, cross_entropy_per_row_vjp,  # noqa: F401
                          selective_log_softmax)

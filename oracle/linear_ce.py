@@ -29,6 +29,7 @@ from typing import Optional, Sequence
 import torch
 
 from oracle.bf16 import round_to_bf16
+from oracle.fp16 import round_to_fp16
 from oracle.ce import count_valid, cross_entropy_rows, reduction_scale
 
 
@@ -48,9 +49,9 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
     """Loss, grad_inputs and grad_weight of the linear cross-entropy, in fp64.
 
     ``grad_weight_accum_dtype='fp32'`` returns the exact fp64 gradients (chunking
-    does not change them); ``'weight'`` returns the chunk-by-chunk bf16 emulation
-    of the weight gradient (``chunk_size`` rows per chunk) and the exact
-    ``grad_inputs``. Returns a dict with ``loss``, ``grad_inputs``,
+    does not change them); ``'weight'`` returns the chunk-by-chunk emulation of
+    the weight gradient in the weight's dtype (bf16, or fp16 for an fp16
+    weight; ``chunk_size`` rows per chunk) and the exact ``grad_inputs``. Returns a dict with ``loss``, ``grad_inputs``,
     ``grad_weight``, ``n_valid``, ``lse`` and ``row_loss``.
     """
     BT, D = inputs.shape
@@ -72,6 +73,7 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
         step = chunk_size
     else:
         raise ValueError(f"unknown grad_weight_accum_dtype {grad_weight_accum_dtype!r}")
+    rnd = round_to_fp16 if weight.dtype == torch.float16 else round_to_bf16
 
     for r0 in range(0, BT, step):
         r1 = min(BT, r0 + step)
@@ -84,7 +86,7 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
         if grad_weight_accum_dtype == "fp32":
             dW.addmm_(G.T, X[r0:r1])                             # exact sum over chunks
         else:
-            dW = round_to_bf16(dW + G.T @ X[r0:r1])              # rounds between chunks
+            dW = rnd(dW + G.T @ X[r0:r1])                        # rounds between chunks
     loss = _finish_loss(row_loss.tolist(), n_valid, reduction)
     return {"loss": loss, "grad_inputs": dX, "grad_weight": dW, "n_valid": n_valid,
             "lse": lse, "row_loss": row_loss}

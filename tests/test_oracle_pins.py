@@ -26,6 +26,7 @@ import oracle
 from oracle import ce as oce
 from oracle import linear_ce as olce
 from oracle.bf16 import round_to_bf16
+from oracle.fp16 import round_to_fp16
 import workloads
 
 torch.set_default_dtype(torch.float64)
@@ -341,6 +342,30 @@ def test_round_to_bf16_matches_format_and_torch_cast():
     assert torch.equal(ours, theirs)
 
 
+def test_round_to_fp16_matches_format_and_torch_cast():
+    one = 1.0
+    cases = {
+        one + 2 ** -11: one,                    # exact tie -> even (1.0)
+        one + 3 * 2 ** -11: one + 2 ** -9,      # tie -> even (mantissa 2)
+        one + 2 ** -11 + 2 ** -20: one + 2 ** -10,
+        2.0 ** -24: 2.0 ** -24,                 # smallest subnormal
+        2.0 ** -26: 0.0,                        # rounds to zero
+        3 * 2.0 ** -26: 2.0 ** -24,             # 0.75 quantum rounds up
+        65504.0: 65504.0,                       # largest finite
+        65519.0: 65504.0,                       # below the overflow midpoint
+        65520.0: math.inf,                      # tie at the midpoint -> even -> overflow
+    }
+    for v, want in cases.items():
+        assert float(round_to_fp16(torch.tensor([v]))[0]) == want, v
+    g = torch.Generator().manual_seed(15)
+    vals = torch.cat([torch.randn(20000, generator=g, dtype=torch.float32) *
+                      torch.exp2(torch.randint(-30, 18, (20000,), generator=g).float()),
+                      torch.tensor([0.0, -0.0, float("inf"), -float("inf")])])
+    ours = round_to_fp16(vals.double())
+    theirs = vals.to(torch.float16).double()
+    assert torch.equal(ours, theirs)
+
+
 def test_weight_mode_emulation():
     X, W, t = workloads.small_linear_ce(48, 8, 13, dtype=torch.bfloat16, n_ignored=4, seed=3)
     exact = oracle.linear_cross_entropy(X, W, t, -100, "mean", 0.0)
@@ -355,6 +380,16 @@ def test_weight_mode_emulation():
     assert not torch.equal(many["grad_weight"], one["grad_weight"])
     assert torch.equal(many["grad_inputs"], exact["grad_inputs"])
     assert many["loss"] == exact["loss"]
+
+
+def test_weight_mode_emulation_follows_the_weight_dtype():
+    X, W, t = workloads.small_linear_ce(48, 8, 13, dtype=torch.float16, n_ignored=4, seed=3)
+    exact = oracle.linear_cross_entropy(X, W, t, -100, "mean", 0.0)
+    one = oracle.linear_cross_entropy(X, W, t, -100, "mean", 0.0, "weight", chunk_size=48)
+    assert torch.equal(one["grad_weight"], round_to_fp16(exact["grad_weight"]))
+    many = oracle.linear_cross_entropy(X, W, t, -100, "mean", 0.0, "weight", chunk_size=8)
+    bound = 6 * 2.0 ** -11 * exact["grad_weight"].abs().max()
+    assert float((many["grad_weight"] - exact["grad_weight"]).abs().max()) <= float(bound)
 
 
 # ---------------------------------------------------------------- golden fixture
