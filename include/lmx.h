@@ -74,8 +74,9 @@ extern "C" {
 #define LMX_API
 #endif
 
-/* Element type of logits / inputs / weight and of their gradients. */
-typedef enum { LMX_F32 = 0, LMX_BF16 = 1 } lmx_dtype;
+/* Element type of logits / inputs / weight and of their gradients (LMX_F16 is
+ * IEEE binary16). */
+typedef enum { LMX_F32 = 0, LMX_BF16 = 1, LMX_F16 = 2 } lmx_dtype;
 
 /* The page's reduction literal: 'mean' or 'sum' (no 'none'). */
 typedef enum { LMX_MEAN = 0, LMX_SUM = 1 } lmx_reduction;
@@ -144,25 +145,28 @@ LMX_API size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype);
  * gradients accumulated chunk by chunk, chunk_size rows per chunk) and
  * "chunked_linear_cross_entropy" (the cross-entropy specialization with
  * ignore_index, reduction, z_loss_multiplier and grad_weight_accum_dtype; bf16
- * matmuls with fp32 accumulator state). 'mean' divides by the number of valid
- * tokens of the whole call, not of each chunk.
+ * or fp16 matmuls with fp32 accumulator state). 'mean' divides by the number
+ * of valid tokens of the whole call, not of each chunk; that 1/N multiplies the
+ * fp32 products, and the 16-bit logits gradient between the matmuls is that of
+ * the summed loss (in fp16, p/N would underflow at large N).
+ * "16-bit" below is the format `dtype` names, for every 16-bit buffer alike.
  *
- *   inputs        [BT, D] bf16, row-major, 16-byte aligned; D % 8 == 0.
+ *   inputs        [BT, D] 16-bit, row-major, 16-byte aligned; D % 8 == 0.
  *   Size limits (LMX_ERR_SIZE beyond them; the GEMMs address 256-row panels
  *   with 32-bit byte offsets): V <= 4194048, D <= 2097088, and at most
  *   4194240 rows per chunk.
- *   weight        [V, D]  bf16, row-major, 16-byte aligned.
+ *   weight        [V, D]  16-bit, row-major, 16-byte aligned.
  *   target        [BT] int64.
- *   dtype         LMX_BF16 (the only one implemented; others give
- *                 LMX_ERR_UNSUPPORTED).
+ *   dtype         LMX_BF16 or LMX_F16 (LMX_F32 gives LMX_ERR_UNSUPPORTED:
+ *                 the matmuls take 16-bit operands).
  *   chunk_size    rows per chunk; 0 picks a size from a 1 GiB budget for the
  *                 chunk's logits; < 0 is LMX_ERR_CHUNK.
  *   accum         LMX_ACC_F32: grad_weight is accumulated in an fp32
  *                 workspace and rounded once; LMX_ACC_WEIGHT: it is
  *                 accumulated in grad_weight itself, rounding after each chunk.
  *   loss          one fp32 on the device.
- *   grad_inputs   [BT, D] bf16 output, 16-byte aligned.
- *   grad_weight   [V, D]  bf16 output, 16-byte aligned.
+ *   grad_inputs   [BT, D] 16-bit output, 16-byte aligned.
+ *   grad_weight   [V, D]  16-bit output, 16-byte aligned.
  *   n_valid, bad_target as for ce_fwd_bwd (may be NULL).
  *   workspace     >= linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum).
  * Outputs must not overlap the inputs (LMX_ERR_ALIAS).
@@ -183,14 +187,16 @@ LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int d
  * linear_loss_logits -- logits of one row chunk for the generic chunked loss.
  *
  * Greyhound functional API page, entry "chunked_linear_loss": inputs @ weight.T
- * evaluated in row chunks; this is one chunk, in bf16 with fp32 accumulation
- * (the page's bf16 matmuls), rounded to nearest even.
+ * evaluated in row chunks; this is one chunk, with 16-bit operands (`dtype`
+ * LMX_BF16 or LMX_F16, the page's bf16/fp16 matmuls) and fp32 accumulation,
+ * rounded to nearest even into the same format.
  *
- *   inputs_c    [rows, D] bf16, 16-byte aligned, D % 8 == 0.
- *   weight      [V, D] bf16, 16-byte aligned.
- *   logits      [rows, ld_logits] bf16 output (ld_logits >= V; columns >= V
+ *   inputs_c    [rows, D] 16-bit, 16-byte aligned, D % 8 == 0.
+ *   weight      [V, D] 16-bit, 16-byte aligned.
+ *   logits      [rows, ld_logits] 16-bit output (ld_logits >= V; columns >= V
  *               are not written), not overlapping the inputs.
- * Limits as for linear_ce (LMX_ERR_SIZE); dtype must be LMX_BF16. No workspace.
+ * Limits as for linear_ce (LMX_ERR_SIZE); LMX_F32 is LMX_ERR_UNSUPPORTED. No
+ * workspace.
  */
 LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows,
                                int64_t D, int64_t V, int dtype, void* logits,
@@ -204,7 +210,7 @@ LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t
  *   grad_inputs[chunk rows] = G_c @ weight,
  *   grad_weight            (+)= G_c^T @ inputs_c,
  * accumulated over the chunks in fp32 (LMX_ACC_F32: a workspace accumulator,
- * rounded to bf16 once, by the last chunk's call) or in grad_weight itself
+ * rounded to the 16-bit format once, by the last chunk's call) or in grad_weight itself
  * (LMX_ACC_WEIGHT: rounded after every chunk), the page's
  * grad_weight_accum_dtype.
  *
@@ -215,12 +221,14 @@ LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t
  * must not be touched in between (chunk 0 stores weight.T there for the later
  * chunks). grad_weight is complete after the call for the last chunk.
  *
- *   inputs_c      [rows, D] bf16 rows of this chunk; rows must be the chunk's
+ *   inputs_c      [rows, D] 16-bit rows of this chunk (`dtype` LMX_BF16 or
+ *                 LMX_F16 for every 16-bit buffer); rows must be the chunk's
  *                 size (c, or what is left of BT for the last one).
- *   grad_logits   [rows, ld_grad] bf16, 16-byte aligned; ld_grad >= V and
+ *   grad_logits   [rows, ld_grad] 16-bit, 16-byte aligned; ld_grad >= V and
  *                 V % 8 == 0 and ld_grad % 8 == 0 (LMX_ERR_ALIGN otherwise).
- *   grad_inputs_c [rows, D] bf16 output for this chunk's rows.
- *   grad_weight   [V, D] bf16 output / accumulator.
+ *                 Used as given: any reduction scale is the caller's.
+ *   grad_inputs_c [rows, D] 16-bit output for this chunk's rows.
+ *   grad_weight   [V, D] 16-bit output / accumulator.
  * Outputs must not overlap the inputs (LMX_ERR_ALIAS); a chunk_index outside
  * [0, nchunks) is LMX_ERR_CHUNK.
  */

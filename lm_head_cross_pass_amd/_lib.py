@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "liblmx.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lmx.h")
 
 # enums of lmx.h
-LMX_F32, LMX_BF16 = 0, 1
+LMX_F32, LMX_BF16, LMX_F16 = 0, 1, 2
 LMX_MEAN, LMX_SUM = 0, 1
 LMX_ACC_F32, LMX_ACC_WEIGHT = 0, 1
 

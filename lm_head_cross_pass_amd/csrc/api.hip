@@ -17,10 +17,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+bool dtype_ok(int dtype) { return dtype == LMX_F32 || dtype == LMX_BF16 || dtype == LMX_F16; }
+
 // One logits row must fit a 32-bit byte offset (row buffer resources and the
 // kernels' per-row offsets are 32-bit), besides V < 2^30.
 bool row_fits(int64_t V, int dtype) {
-  const int64_t eb = dtype == LMX_BF16 ? 2 : 4;
+  const int64_t eb = dtype == LMX_F32 ? 4 : 2;
   return V > 0 && V < (int64_t{1} << 30) && V * eb <= INT32_MAX - 64;
 }
 
@@ -67,7 +69,7 @@ const char* lmx_status_string(int status) {
 }
 
 size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype) {
-  if (B < 0 || (dtype != LMX_F32 && dtype != LMX_BF16) || !row_fits(V, dtype)) return 0;
+  if (B < 0 || !dtype_ok(dtype) || !row_fits(V, dtype)) return 0;
   return lmx::ce_workspace_layout(B).total;
 }
 
@@ -78,9 +80,9 @@ int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int
   if (loss == nullptr || workspace == nullptr) return LMX_ERR_NULL;
   if (B > 0 && (logits == nullptr || target == nullptr)) return LMX_ERR_NULL;
   if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
-  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
   if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
-  const int eb = dtype == LMX_BF16 ? 2 : 4;
+  const int eb = dtype == LMX_F32 ? 4 : 2;
   if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
   const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
   const uintptr_t pl = reinterpret_cast<uintptr_t>(logits);
@@ -123,8 +125,8 @@ static int rows_forward(const void* logits, const int64_t* target, int64_t B, in
   if (workspace == nullptr) return LMX_ERR_NULL;
   if (B > 0 && (logits == nullptr || target == nullptr || out == nullptr)) return LMX_ERR_NULL;
   if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
-  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
-  const int eb = dtype == LMX_BF16 ? 2 : 4;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
+  const int eb = dtype == LMX_F32 ? 4 : 2;
   if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
   const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
   if (reinterpret_cast<uintptr_t>(logits) % eb != 0 ||
@@ -179,8 +181,8 @@ int ce_loss_rows_vjp(const void* logits, const int64_t* target, const float* los
                 g == nullptr || grad_logits == nullptr))
     return LMX_ERR_NULL;
   if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
-  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
-  const int eb = dtype == LMX_BF16 ? 2 : 4;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
+  const int eb = dtype == LMX_F32 ? 4 : 2;
   if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
   const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
   const uintptr_t pl = reinterpret_cast<uintptr_t>(logits);
@@ -209,7 +211,7 @@ int ce_loss_rows_vjp(const void* logits, const int64_t* target, const float* los
 size_t linear_loss_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
                                    int64_t chunk_size, int accum) {
   if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0) return 0;
-  if (dtype != LMX_BF16) return 0;
+  if (dtype != LMX_BF16 && dtype != LMX_F16) return 0;
   if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return 0;
   if (V > kLinMaxV || D > kLinMaxD) return 0;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
@@ -224,8 +226,8 @@ int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, i
   if (rows < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || rows > kLinMaxChunk ||
       ld_logits < V)
     return LMX_ERR_SIZE;
-  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
-  if (dtype != LMX_BF16) return LMX_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
+  if (dtype == LMX_F32) return LMX_ERR_UNSUPPORTED;
   if (D % 8 != 0 || reinterpret_cast<uintptr_t>(inputs_c) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(weight) % 16 != 0 || reinterpret_cast<uintptr_t>(logits) % 2 != 0)
     return LMX_ERR_ALIGN;
@@ -233,7 +235,7 @@ int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, i
   if (rows > 0 && (overlaps(logits, lb, inputs_c, static_cast<size_t>(rows) * D * 2) ||
                    overlaps(logits, lb, weight, static_cast<size_t>(V) * D * 2)))
     return LMX_ERR_ALIAS;
-  return lmx::linear_loss_logits_enqueue(static_cast<const uint16_t*>(inputs_c),
+  return lmx::linear_loss_logits_enqueue(dtype, static_cast<const uint16_t*>(inputs_c),
                                          static_cast<const uint16_t*>(weight),
                                          static_cast<int>(rows), static_cast<int>(D),
                                          static_cast<int>(V), static_cast<uint16_t*>(logits),
@@ -250,9 +252,9 @@ int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad
   if (BT <= 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || ld_grad < V)
     return LMX_ERR_SIZE;
   if (chunk_size < 0) return LMX_ERR_CHUNK;
-  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
   if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return LMX_ERR_ENUM;
-  if (dtype != LMX_BF16) return LMX_ERR_UNSUPPORTED;
+  if (dtype == LMX_F32) return LMX_ERR_UNSUPPORTED;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
   if (c > kLinMaxChunk) return LMX_ERR_SIZE;
   const int64_t nchunks = (BT + c - 1) / c;
@@ -275,6 +277,7 @@ int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad
   const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
   lmx::LinearLossChunk p{};
+  p.dtype = dtype;
   p.xc = static_cast<const uint16_t*>(inputs_c);
   p.w = static_cast<const uint16_t*>(weight);
   p.g = static_cast<const uint16_t*>(grad_logits);
@@ -299,7 +302,7 @@ int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size) {
 size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
                                  int64_t chunk_size, int accum) {
   if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0) return 0;
-  if (dtype != LMX_BF16) return 0;
+  if (dtype != LMX_BF16 && dtype != LMX_F16) return 0;
   if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return 0;
   if (V > kLinMaxV || D > kLinMaxD) return 0;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
@@ -318,10 +321,10 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
     return LMX_ERR_NULL;
   if (BT < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD) return LMX_ERR_SIZE;
   if (chunk_size < 0) return LMX_ERR_CHUNK;
-  if (dtype != LMX_F32 && dtype != LMX_BF16) return LMX_ERR_ENUM;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
   if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
   if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return LMX_ERR_ENUM;
-  if (dtype != LMX_BF16) return LMX_ERR_UNSUPPORTED;
+  if (dtype == LMX_F32) return LMX_ERR_UNSUPPORTED;
   if (!mul_fits(BT, D, 2) || !mul_fits(V, D, 4) || !mul_fits(BT, V, 2)) return LMX_ERR_SIZE;
   if (D % 8 != 0) return LMX_ERR_ALIGN;
   for (const void* q : {inputs, weight, static_cast<const void*>(grad_inputs),
@@ -340,7 +343,8 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
   if (c > kLinMaxChunk) return LMX_ERR_SIZE;
   const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
-  lmx::LinearCeParams p;
+  lmx::LinearCeParams p{};
+  p.dtype = dtype;
   p.x = static_cast<const uint16_t*>(inputs);
   p.w = static_cast<const uint16_t*>(weight);
   p.target = target;

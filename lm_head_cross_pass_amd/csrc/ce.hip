@@ -20,6 +20,8 @@
 //   workgroup walks rows blockIdx, blockIdx + gridDim, ...;
 // * rows too wide for the register file fall back to a streaming kernel that
 //   reads the row twice (the second read usually hits L2 / MALL).
+#include <type_traits>
+
 #include "internal.h"
 
 namespace lmx {
@@ -70,19 +72,52 @@ template <> struct Elem<uint16_t> {  // bf16 stored as raw 16-bit patterns
   }
 };
 
+// fp16 logits: raw 16-bit patterns, tagged by a distinct 2-byte type.
+struct Half {
+  uint16_t bits;
+};
+template <> struct Elem<Half> {
+  static constexpr int kPerChunk = 8;
+  __device__ static void unpack(const u32x4& c, float* x) {
+    x[0] = f16_lo(c.x); x[1] = f16_hi(c.x); x[2] = f16_lo(c.y); x[3] = f16_hi(c.y);
+    x[4] = f16_lo(c.z); x[5] = f16_hi(c.z); x[6] = f16_lo(c.w); x[7] = f16_hi(c.w);
+  }
+  __device__ static u32x4 pack(const float* g) {
+    return u32x4{pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3]),
+                 pack_f16x2(g[4], g[5]), pack_f16x2(g[6], g[7])};
+  }
+  __device__ static float load_one(uintptr_t addr) {
+    return f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(addr));
+  }
+  __device__ static void store_one(__amdgpu_buffer_rsrc_t r, int off, float g) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_f16_bits(g), r, off, 0, 0);
+  }
+  __device__ static void set_neg_inf(u32x4& c, int e) {
+    const uint32_t w = c[e >> 1];
+    c[e >> 1] = (e & 1) ? ((w & 0x0000ffffu) | 0xfc000000u) : ((w & 0xffff0000u) | 0x0000fc00u);
+  }
+};
+
 // Makes the compiler forget what it knows about a register-resident chunk, so
 // each sweep re-widens the packed data instead of keeping a widened copy of the
 // whole row alive (which would not fit the register file).
 __device__ __forceinline__ void launder(u32x4& c) { asm volatile("" : "+v"(c)); }
 
-// exp(x - m) * 2^-extra, evaluated as a base-2 exponential. fp32 logits take
-// the difference x - m first (exact when x is near the max, where the
-// probabilities are large), which keeps the gradient within a few fp32 ulps
-// of the exact value; bf16 logits fold everything into one fma, whose
-// rounding is far below the bf16 output's.
+// Whether exponentials fold the shift into one fma (bf16 only). fp32 and fp16
+// logits take the difference x - m first: it is exact when x is near the max,
+// where the probabilities are large, so the result stays within a few fp32
+// ulps whatever the logits' offset. The folded form rounds m log2(e) once, an
+// error of up to half an fp32 ulp of |m| log2(e) in every exponent: far below
+// a bf16 output's rounding, but visible in fp16 outputs and fp32 losses once
+// |m| reaches the thousands.
+template <typename T>
+constexpr bool kFoldShift = std::is_same<T, uint16_t>::value;
+
+// exp(x - m) * 2^-extra, evaluated as a base-2 exponential (comb = m log2(e)
+// + extra, used by the folded form).
 template <typename T>
 __device__ __forceinline__ float shifted_exp2(float x, float m, float extra, float comb) {
-  if constexpr (sizeof(T) == 4) {
+  if constexpr (!kFoldShift<T>) {
     return exp2_fast(__builtin_fmaf(x - m, kLog2e, -extra));
   } else {
     return exp2_fast(__builtin_fmaf(x, kLog2e, -comb));   // comb = m * log2(e) + extra
@@ -525,8 +560,9 @@ __global__ __launch_bounds__(kVjpThreads) void ce_vjp_kernel(VjpParams p) {
   }
   const float g = p.g[row];
   const float xt = Elem<T>::load_one(base + (static_cast<uintptr_t>(row) * p.V + t) * sizeof(T));
-  // lse = loss + x[t] without a rounding: fp32 logits take x - lse in fp64
-  // (the float loss input then carries the only rounding), bf16 logits one fma
+  // lse = loss + x[t] without a rounding: fp32 and fp16 logits take x - lse in
+  // fp64 (the float loss input then carries the only rounding), bf16 logits
+  // one fma
   const double lse_d = static_cast<double>(p.loss[row]) + static_cast<double>(xt);
   const float lseL = static_cast<float>(lse_d * static_cast<double>(kLog2e));
   const int tpos = r.lead + static_cast<int>(t);
@@ -545,7 +581,7 @@ __global__ __launch_bounds__(kVjpThreads) void ce_vjp_kernel(VjpParams p) {
       Elem<T>::unpack(d[k], x);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        if constexpr (sizeof(T) == 4) {
+        if constexpr (!kFoldShift<T>) {
           const float dx = static_cast<float>(static_cast<double>(x[e]) - lse_d);
           gv[e] = g * exp2_fast(dx * kLog2e);
         } else {
@@ -627,13 +663,14 @@ int finish_enqueue(const float* row_loss, int64_t B, const int64_t* n_ws, int re
 
 int ce_rows_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
   if (p.B > 0) {
-    const int eb = dtype == LMX_BF16 ? 2 : 4;
+    const int eb = dtype == LMX_F32 ? 4 : 2;
     const int64_t need = ce_max_row_chunks(reinterpret_cast<uintptr_t>(p.logits), p.V, p.ld, eb);
     int n = 0;
     const bool g = p.grad != nullptr;
-    const RowKernel* ks = dtype == LMX_BF16
-                              ? (g ? row_kernels<uint16_t, true>(&n) : row_kernels<uint16_t, false>(&n))
-                              : (g ? row_kernels<float, true>(&n) : row_kernels<float, false>(&n));
+    const RowKernel* ks =
+        dtype == LMX_BF16 ? (g ? row_kernels<uint16_t, true>(&n) : row_kernels<uint16_t, false>(&n))
+        : dtype == LMX_F16 ? (g ? row_kernels<Half, true>(&n) : row_kernels<Half, false>(&n))
+                           : (g ? row_kernels<float, true>(&n) : row_kernels<float, false>(&n));
     const RowKernel* pick = &ks[n - 1];
     for (int i = 0; i < n; ++i) {
       if (ks[i].capacity == 0 || ks[i].capacity >= need) { pick = &ks[i]; break; }
@@ -660,8 +697,9 @@ int ce_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
 int ce_vjp_enqueue(const VjpParams& p, int dtype, hipStream_t stream) {
   if (p.B == 0) return LMX_OK;
   if (p.B > INT32_MAX) return LMX_ERR_SIZE;
-  const void* fn = dtype == LMX_BF16 ? reinterpret_cast<const void*>(&ce_vjp_kernel<uint16_t>)
-                                     : reinterpret_cast<const void*>(&ce_vjp_kernel<float>);
+  const void* fn = dtype == LMX_BF16  ? reinterpret_cast<const void*>(&ce_vjp_kernel<uint16_t>)
+                   : dtype == LMX_F16 ? reinterpret_cast<const void*>(&ce_vjp_kernel<Half>)
+                                      : reinterpret_cast<const void*>(&ce_vjp_kernel<float>);
   VjpParams pc = p;
   void* args[] = {&pc};
   if (hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.B)), dim3(kVjpThreads), args, 0,

@@ -32,6 +32,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return static_cast<uint16_t>(pack_bf16x2(x, 0.f) & 0xffffu);
 }
 
+// IEEE binary16 <-> fp32: hardware converts (v_cvt_f32_f16, and the
+// round-to-nearest-even v_cvt_f16_f32 behind the _Float16 cast).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2_t, w)[0]);
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2_t, w)[1]);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// 16-bit element formats of the linear path, as tags for templates.
+struct Bf16 {
+  __device__ static float widen(uint16_t h) { return bf16_bits_to_f32(h); }
+  __device__ static uint16_t narrow(float x) { return f32_to_bf16_bits(x); }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+};
+struct F16 {
+  __device__ static float widen(uint16_t h) { return f16_bits_to_f32(h); }
+  __device__ static uint16_t narrow(float x) { return f32_to_f16_bits(x); }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+};
+
 // v_exp_f32 / v_log_f32 work in base 2.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }

@@ -1,9 +1,10 @@
-// bf16 MFMA GEMM for gfx950: C[M, N] = A[M, K] * B[N, K]^T, fp32 accumulation.
+// bf16 / fp16 MFMA GEMM for gfx950: C[M, N] = A[M, K] * B[N, K]^T, fp32
+// accumulation.
 //
 // Both operands are K-contiguous (row-major with leading dimensions lda, ldb,
 // multiples of 8 elements, 16-byte aligned), which is the layout the
-// v_mfma_f32_32x32x16_bf16 operands want: each lane supplies 8 consecutive k
-// values of one row of A (or of B^T).
+// v_mfma_f32_32x32x16_bf16 / _f16 operands want: each lane supplies 8
+// consecutive k values of one row of A (or of B^T).
 //
 // Work decomposition:
 // * a workgroup computes a BM x BN tile: 512 threads (8 waves as 2 x 4) for
@@ -38,7 +39,24 @@
 namespace lmx {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// The MFMA of an element format (Bf16 / F16 of common.h): fragments travel
+// as raw 16-byte vectors and are reinterpreted here.
+template <typename E> struct Mfma;
+template <> struct Mfma<Bf16> {
+  __device__ static f32x16_t run(const u32x4& a, const u32x4& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<F16> {
+  __device__ static f32x16_t run(const u32x4& a, const u32x4& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 #ifndef LMX_GEMM_BK
@@ -195,24 +213,23 @@ __device__ __forceinline__ void gemm_copy_stage(char* smem, __amdgpu_buffer_rsrc
 template <typename C, int KK>
 __device__ __forceinline__ void gemm_load_frags(const char* smem, const int* a_off,
                                                 const int* b_off, int stage_bytes,
-                                                bf16x8_t* af, bf16x8_t* bfr) {
+                                                u32x4* af, u32x4* bfr) {
   const int flip = stage_bytes | (KK << 5);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
-    af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(smem + (a_off[i] ^ flip)));
+    af[i] = *reinterpret_cast<const u32x4*>(smem + (a_off[i] ^ flip));
 #pragma unroll
   for (int j = 0; j < C::FN; ++j)
-    bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(smem + (b_off[j] ^ flip)));
+    bfr[j] = *reinterpret_cast<const u32x4*>(smem + (b_off[j] ^ flip));
 }
 
-template <typename C>
-__device__ __forceinline__ void gemm_mfma_slice(f32x16_t (&acc)[C::FM][C::FN],
-                                                const bf16x8_t* af, const bf16x8_t* bfr) {
+template <typename C, typename E>
+__device__ __forceinline__ void gemm_mfma_slice(f32x16_t (&acc)[C::FM][C::FN], const u32x4* af,
+                                                const u32x4* bfr) {
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<E>::run(af[i], bfr[j], acc[i][j]);
 }
 
 // Schedule hints for one k slice (FM + FN fragment reads of slice k + 1, FM x FN
@@ -241,7 +258,8 @@ __device__ __forceinline__ void gemm_interleave_hint() {
   }
 }
 
-template <int BM, int BN, typename Epi, int SCHED>
+// E: the operands' 16-bit element format (Bf16 or F16 of common.h).
+template <int BM, int BN, typename Epi, int SCHED, typename E>
 __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(GemmShape g,
                                                                             Epi epi) {
   using C = GemmCfg<BM, BN>;
@@ -305,7 +323,7 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     const int r = wn * C::WN + j * 32 + frag_row;
     b_off[j] = C::B_BASE + r * C::ROWB + ((frag_half ^ lds_swz<C::CPR>(r)) << 4);
   }
-  bf16x8_t fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  u32x4 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
   static_assert(kGemmBK == 32 || kGemmBK == 64, "two or four 16-wide k slices per step");
   constexpr int AHEAD = kGemmStages - 1;   // steps in flight ahead of the one computed
 
@@ -334,17 +352,17 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
                          __builtin_amdgcn_readfirstlane((t + AHEAD) % kGemmStages), wave, g.K);
     }
     gemm_load_frags<C, 1>(smem, a_off, b_off, cur_bytes, fa1, fb1);
-    gemm_mfma_slice<C>(acc, fa0, fb0);
+    gemm_mfma_slice<C, E>(acc, fa0, fb0);
     gemm_interleave_hint<C, SCHED>();
     if constexpr (kGemmBK == 64) {
       gemm_load_frags<C, 2>(smem, a_off, b_off, cur_bytes, fa0, fb0);
-      gemm_mfma_slice<C>(acc, fa1, fb1);
+      gemm_mfma_slice<C, E>(acc, fa1, fb1);
       gemm_interleave_hint<C, SCHED>();
       gemm_load_frags<C, 3>(smem, a_off, b_off, cur_bytes, fa1, fb1);
-      gemm_mfma_slice<C>(acc, fa0, fb0);
+      gemm_mfma_slice<C, E>(acc, fa0, fb0);
       gemm_interleave_hint<C, SCHED>();
     }
-    gemm_mfma_slice<C>(acc, fa1, fb1);
+    gemm_mfma_slice<C, E>(acc, fa1, fb1);
     if (ks + 1 < ke) {
       // step ks + 1 landed: the copies issued after it (up to AHEAD - 1 steps)
       // may still be in flight

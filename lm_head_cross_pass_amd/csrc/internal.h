@@ -61,8 +61,9 @@ CeWorkspace ce_workspace_layout(int64_t B);
 
 // Linear cross-entropy.
 struct LinearCeParams {
-  const uint16_t* x;        // [BT, D] bf16
-  const uint16_t* w;        // [V, D] bf16
+  int dtype;                // LMX_BF16 or LMX_F16 (inputs, weight and the gradients)
+  const uint16_t* x;        // [BT, D]
+  const uint16_t* w;        // [V, D]
   const int64_t* target;    // [BT]
   int64_t BT, D, V;
   int64_t ignore_index;
@@ -71,8 +72,8 @@ struct LinearCeParams {
   int64_t chunk;            // rows per chunk (resolved, > 0)
   int accum;                // LMX_ACC_F32 / LMX_ACC_WEIGHT
   float* loss;
-  uint16_t* grad_x;         // [BT, D] bf16
-  uint16_t* grad_w;         // [V, D] bf16
+  uint16_t* grad_x;         // [BT, D]
+  uint16_t* grad_w;         // [V, D]
   int64_t* n_valid_user;
   int32_t* bad_user;
 };
@@ -94,19 +95,20 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream);
 
 // Generic chunked linear loss (the caller's loss and logits gradient per chunk):
 // logits of one chunk, then its gradients.
-int linear_loss_logits_enqueue(const uint16_t* xc, const uint16_t* w, int rows, int D, int V,
-                               uint16_t* logits, int64_t ld_logits, hipStream_t stream);
+int linear_loss_logits_enqueue(int dtype, const uint16_t* xc, const uint16_t* w, int rows, int D,
+                               int V, uint16_t* logits, int64_t ld_logits, hipStream_t stream);
 struct LinearLossChunk {
-  const uint16_t* xc;       // [rows, D] bf16
-  const uint16_t* w;        // [V, D] bf16
-  const uint16_t* g;        // [rows, ld_g] bf16: d(loss)/d(logits) of the chunk
+  int dtype;                // LMX_BF16 or LMX_F16
+  const uint16_t* xc;       // [rows, D]
+  const uint16_t* w;        // [V, D]
+  const uint16_t* g;        // [rows, ld_g]: d(loss)/d(logits) of the chunk
   int64_t ld_g;
   int rows;
   int64_t BT, D, V, chunk;  // chunk: rows per chunk of the whole pass (resolved)
   int accum;
   int64_t index;            // chunk number within the pass
-  uint16_t* grad_xc;        // [rows, D] bf16
-  uint16_t* grad_w;         // [V, D] bf16
+  uint16_t* grad_xc;        // [rows, D]
+  uint16_t* grad_w;         // [V, D]
 };
 int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws, hipStream_t stream);
 

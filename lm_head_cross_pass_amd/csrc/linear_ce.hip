@@ -8,26 +8,32 @@
 // Per chunk of C rows (r0 .. r0 + C'):
 //   1. X_c^T into its columns of X^T [D, ldk]          transpose
 //   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM
-//   3. the cross-entropy row kernel on Z, in place: loss terms and
-//      G = scale ((1 + 2 z lse) softmax - onehot)      same kernel as ce_fwd_bwd
+//   3. the cross-entropy row kernel on Z, in place: loss terms and the
+//      gradient of the summed loss, G = (1 + 2 z lse) softmax - onehot
+//                                                      same kernel as ce_fwd_bwd
 //   4. G^T into its columns of G^T [ldv, ldk]          transpose
-//   5. grad_inputs[r0:] = G W                          MFMA GEMM (split-K if the
+//   5. grad_inputs[r0:] = s G W                        MFMA GEMM (split-K if the
 //                                                      tile count cannot fill the chip)
-//   6. dW (+)= G^T X_c                                 MFMA GEMM, accumulate epilogue
+//   6. dW (+)= s G^T X_c                               MFMA GEMM, accumulate epilogue
+// where s is 1/N for the mean and 1 for the sum, applied to the fp32
+// accumulators in the epilogues rather than to G: G is held in the 16-bit
+// input format, and for fp16 the mean's scaled probabilities p/N would fall
+// below its smallest subnormal (2^-24) at the batch sizes of the workload.
 // Finally the fixed-order loss reduction. In 'fp32' accumulation dW lives in
-// an fp32 workspace and the last product's epilogue writes the rounded bf16
+// an fp32 workspace and the last product's epilogue writes the rounded 16-bit
 // result; there step 6 runs once per group of chunks (as many as 1 GiB of G^T
 // holds: two at a vocabulary of 128256 and chunks of 2048), on the group's
 // columns of G^T and X^T together (K = group ldc, ldk = group ldc; a last,
 // partial group runs on the chunks it has), which divides the passes over
 // the fp32 accumulator by the group size. In
-// 'weight' accumulation the bf16 grad_weight itself is updated per chunk
+// 'weight' accumulation the 16-bit grad_weight itself is updated per chunk
 // (rounded to nearest even after each chunk, as the accumulation mode
 // prescribes; ldk = ldc).
 //
-// The logits and G are kept in bf16 between steps, as bf16 matmuls produce
-// them; the cross-entropy of a chunk is computed in fp32 from the rounded
-// logits, so G is the cross-entropy gradient of the bf16 logits.
+// The logits and G are kept in the inputs' 16-bit format (bf16 or fp16)
+// between steps, as the matmuls produce and consume them; the cross-entropy of
+// a chunk is computed in fp32 from the rounded logits, so G is the
+// cross-entropy gradient of the rounded logits.
 #include "gemm.h"
 #include "internal.h"
 
@@ -46,18 +52,28 @@ int64_t round_up64(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // ------------------------------------------------------------------ epilogues
 
-// Steps 2 and 5: a bf16 output tile (logits, grad_inputs rows), or fp32
-// split-K partials.
-struct EpiBf16 {
+// Steps 2 and 5: a 16-bit output tile in the element format E (logits,
+// grad_inputs rows), or fp32 split-K partials.
+// 1 / n for a positive count, else 1 (no count, or no valid rows: G is zero).
+__device__ __forceinline__ float count_scale(const int64_t* n) {
+  if (n == nullptr) return 1.0f;
+  const int64_t v = *n;
+  return v > 0 ? 1.0f / static_cast<float>(v) : 1.0f;
+}
+
+template <typename E>
+struct EpiOut {
   uint16_t* out;
   int64_t ldo;
-  float* partial;   // [ksplit][M][ldp]
+  float* partial;        // [ksplit][M][ldp]
   int64_t ldp;
+  const int64_t* mean_count;   // non-null: scale the products by 1 / *mean_count
 
   template <int BM, int BN, int FM, int FN>
   __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int split,
                       const GemmShape& g, uint16_t*) {
     const bool direct = g.ksplit == 1;
+    const float s = count_scale(mean_count);
     const __amdgpu_buffer_rsrc_t ro =
         direct ? rows_rsrc(out, m0, g.M - m0, BM, ldo * 2)
                : rows_rsrc(partial + static_cast<int64_t>(split) * g.M * ldp, m0, g.M - m0, BM,
@@ -72,10 +88,10 @@ struct EpiBf16 {
         for (int r = 0; r < 16; ++r) {
           const int row = ac.row(i, r);   // tile-local; rows >= M fall outside the resource
           if (direct) {
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[i][j][r]), ro,
+            __builtin_amdgcn_raw_buffer_store_b16(E::narrow(s * acc[i][j][r]), ro,
                                                   (row * static_cast<int>(ldo) + col) * 2, 0, 0);
           } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro,
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * acc[i][j][r]), ro,
                                                   (row * static_cast<int>(ldp) + col) * 4, 0, 0);
           }
         }
@@ -83,26 +99,29 @@ struct EpiBf16 {
   }
 };
 
-enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToBf16 = 2, kDwStoreBf16 = 3, kDwAddBf16 = 4 };
+// grad_weight epilogue modes; "W16" is the weight's 16-bit format (bf16 / fp16).
+enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToW16 = 2, kDwStoreW16 = 3, kDwAddW16 = 4 };
 
 // Step 6: grad_weight accumulation. Read-modify-write epilogues issue all the
 // reads of an accumulator column before any add, so the memory latency is paid
 // once per column (this measured faster than fire-and-forget buffer atomics).
+template <typename E>
 struct EpiDw {
   float* acc32;     // [V][ld] fp32 accumulator ('fp32' mode)
-  uint16_t* out16;  // [V][ld] bf16 grad_weight
+  uint16_t* out16;  // [V][ld] grad_weight in the weight's format E
   int64_t ld;
   int mode;
+  const int64_t* mean_count;   // non-null: scale the products by 1 / *mean_count
 
   template <int MODE, int FM, int FN>
   __device__ void apply(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int n0, const GemmShape& g,
-                        __amdgpu_buffer_rsrc_t r32, __amdgpu_buffer_rsrc_t r16) {
+                        __amdgpu_buffer_rsrc_t r32, __amdgpu_buffer_rsrc_t r16, float s) {
     const int ldi = static_cast<int>(ld);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + ac.col(j);
       if (col >= g.N) continue;
-      if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToBf16 || MODE == kDwAddBf16) {
+      if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToW16 || MODE == kDwAddW16) {
         // read-modify-write: all FM x 16 reads of this column first, so their
         // latency is paid once per column instead of once per element
         float old[FM * 16];
@@ -111,10 +130,10 @@ struct EpiDw {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int e = ac.row(i, r) * ldi + col;
-            if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToBf16) {
+            if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToW16) {
               old[i * 16 + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r32, e * 4, 0, 0));
             } else {
-              old[i * 16 + r] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0));
+              old[i * 16 + r] = E::widen(__builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0));
             }
           }
 #pragma unroll
@@ -122,11 +141,11 @@ struct EpiDw {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int e = ac.row(i, r) * ldi + col;
-            const float v = old[i * 16 + r] + acc[i][j][r];
+            const float v = old[i * 16 + r] + s * acc[i][j][r];
             if constexpr (MODE == kDwAddF32) {
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r32, e * 4, 0, 0);
             } else {
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r16, e * 2, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(E::narrow(v), r16, e * 2, 0, 0);
             }
           }
       } else {
@@ -135,11 +154,11 @@ struct EpiDw {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int e = ac.row(i, r) * ldi + col;   // tile-local row; rows >= M are dropped
-            const float v = acc[i][j][r];
+            const float v = s * acc[i][j][r];
             if constexpr (MODE == kDwStoreF32) {
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r32, e * 4, 0, 0);
             } else {
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r16, e * 2, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(E::narrow(v), r16, e * 2, 0, 0);
             }
           }
       }
@@ -151,12 +170,13 @@ struct EpiDw {
                       const GemmShape& g, uint16_t*) {
     const __amdgpu_buffer_rsrc_t r32 = rows_rsrc(acc32, m0, g.M - m0, BM, ld * 4);
     const __amdgpu_buffer_rsrc_t r16 = rows_rsrc(out16, m0, g.M - m0, BM, ld * 2);
+    const float s = count_scale(mean_count);
     switch (mode) {
-      case kDwStoreF32: apply<kDwStoreF32>(acc, ac, n0, g, r32, r16); break;
-      case kDwAddF32: apply<kDwAddF32>(acc, ac, n0, g, r32, r16); break;
-      case kDwAddF32ToBf16: apply<kDwAddF32ToBf16>(acc, ac, n0, g, r32, r16); break;
-      case kDwStoreBf16: apply<kDwStoreBf16>(acc, ac, n0, g, r32, r16); break;
-      default: apply<kDwAddBf16>(acc, ac, n0, g, r32, r16); break;
+      case kDwStoreF32: apply<kDwStoreF32>(acc, ac, n0, g, r32, r16, s); break;
+      case kDwAddF32: apply<kDwAddF32>(acc, ac, n0, g, r32, r16, s); break;
+      case kDwAddF32ToW16: apply<kDwAddF32ToW16>(acc, ac, n0, g, r32, r16, s); break;
+      case kDwStoreW16: apply<kDwStoreW16>(acc, ac, n0, g, r32, r16, s); break;
+      default: apply<kDwAddW16>(acc, ac, n0, g, r32, r16, s); break;
     }
   }
 };
@@ -205,7 +225,8 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
-// grad_inputs rows = bf16(sum over splits of the fp32 partials), fixed order.
+// grad_inputs rows = E(sum over splits of the fp32 partials), fixed order.
+template <typename E>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
                                                             int ksplit, int M, int N,
                                                             int64_t ldp,
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         partial + (static_cast<int64_t>(s) * M + row) * ldp + col);
     a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
   }
-  uint2 o = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+  uint2 o = make_uint2(E::pack2(a[0], a[1]), E::pack2(a[2], a[3]));
   *reinterpret_cast<uint2*>(out + static_cast<int64_t>(row) * ldo + col) = o;
 }
 
@@ -235,17 +256,17 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* p, int64_t n) {
 
 // SCHED selects the main loop's schedule hints for the large tile (see
 // gemm_interleave_hint); the small tile always uses schedule 0.
-template <int SCHED, typename Epi>
+template <int SCHED, typename E, typename Epi>
 int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream) {
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   if (tile == kTileL) {
     constexpr int threads = GemmCfg<kTileL, kTileL>::THREADS;
-    hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi, SCHED>), dim3(blocks),
+    hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi, SCHED, E>), dim3(blocks),
                        dim3(threads), 0, stream, g, epi);
   } else {
     constexpr int threads = GemmCfg<kTileS, kTileS>::THREADS;
-    hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi, 0>), dim3(blocks), dim3(threads),
+    hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi, 0, E>), dim3(blocks), dim3(threads),
                        0, stream, g, epi);
   }
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
@@ -305,19 +326,21 @@ int dx_ksplit(int64_t C, int64_t D, int64_t ldv) {
 }
 
 // grad_inputs rows of one chunk: G [rows, lda_g] times W, with W^T [D, ldv] as
-// the K-contiguous operand over K = k_len vocabulary columns; split-K partials
-// in dxp when the layout chose splits.
+// the K-contiguous operand over K = k_len vocabulary columns, scaled by
+// 1 / *mean_count when that is given; split-K partials in dxp when the layout
+// chose splits.
+template <typename E>
 int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_t* wt,
                       int64_t ldv, int rows, int D, int64_t chunk, int ksplit, float* dxp,
-                      uint16_t* gx, int64_t ldx, hipStream_t stream) {
+                      uint16_t* gx, int64_t ldx, const int64_t* mean_count, hipStream_t stream) {
   const int tile = pick_tile(chunk, D, 2);   // the tile the workspace was sized for
   GemmShape gs = make_shape(g, lda_g, wt, ldv, rows, D, D, k_len, ksplit, tile);
-  EpiBf16 e{gx, ldx, dxp, D};
-  int st = launch_gemm<1>(gs, tile, e, stream);
+  EpiOut<E> e{gx, ldx, dxp, D, mean_count};
+  int st = launch_gemm<1, E>(gs, tile, e, stream);
   if (st != LMX_OK) return st;
   if (gs.ksplit > 1) {
     const int64_t total = static_cast<int64_t>(rows) * D / 4;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+    hipLaunchKernelGGL(splitk_reduce_kernel<E>, dim3(static_cast<unsigned>((total + 255) / 256)),
                        dim3(256), 0, stream, dxp, gs.ksplit, rows, D, static_cast<int64_t>(D),
                        gx, ldx);
     if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
@@ -326,13 +349,16 @@ int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_
 }
 
 // grad_weight product G^T X over K columns of G^T [V, ldk] and X^T [D, ldk],
-// stored or accumulated according to `mode`.
+// scaled by 1 / *mean_count when that is given, stored or accumulated
+// according to `mode`.
+template <typename E>
 int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int K, int V, int D,
-                        float* dw, uint16_t* gw, int64_t ldw, int mode, hipStream_t stream) {
+                        float* dw, uint16_t* gw, int64_t ldw, int mode,
+                        const int64_t* mean_count, hipStream_t stream) {
   const int tile = pick_tile(V, D);
   GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
-  EpiDw e{dw, gw, ldw, mode};
-  return launch_gemm<1>(gs, tile, e, stream);
+  EpiDw<E> e{dw, gw, ldw, mode, mean_count};
+  return launch_gemm<1, E>(gs, tile, e, stream);
 }
 
 }  // namespace
@@ -389,7 +415,8 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   return w;
 }
 
-int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
+template <typename E>
+int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
   const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum);
   char* ws = static_cast<char*>(ws_base);
   int64_t* n_ws = reinterpret_cast<int64_t*>(ws + wl.n_valid_off);
@@ -402,6 +429,7 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
   const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
   const int64_t ldv = wl.ldv, ldc = wl.ldc, ldk = wl.ldk, grp = wl.dw_group;
+  const int64_t* mean_count = p.reduction == LMX_MEAN ? n_ws : nullptr;
 
   int st = count_enqueue(p.target, p.BT, p.V, p.ignore_index, n_ws, p.n_valid_user, p.bad_user,
                          stream);
@@ -428,8 +456,8 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
     {
       const int tile = pick_tile(rows, ldv);
       GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
-      EpiBf16 e{z, ldv, nullptr, 0};
-      st = launch_gemm<1>(g, tile, e, stream);
+      EpiOut<E> e{z, ldv, nullptr, 0, nullptr};
+      st = launch_gemm<1, E>(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
     // 3. cross-entropy of the chunk rows, G written over Z, loss terms
@@ -443,18 +471,19 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       cp.ld = ldv;
       cp.ignore_index = p.ignore_index;
       cp.z = p.z;
-      cp.reduction = p.reduction;
+      cp.reduction = LMX_SUM;   // the mean's 1/N enters in steps 5 and 6
       cp.n_valid_ws = n_ws;
       cp.row_loss = row_loss + r0;
-      st = ce_rows_enqueue(cp, LMX_BF16, stream);
+      st = ce_rows_enqueue(cp, p.dtype, stream);
       if (st != LMX_OK) return st;
     }
     // 4. G^T for the grad_weight product
     st = transpose_pad(z, ldv, rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
     // 5. grad_inputs rows
-    st = chunk_grad_inputs(z, ldv, static_cast<int>(ldv), wt, ldv, rows, D, p.chunk,
-                           static_cast<int>(wl.ksplit), dxp, p.grad_x + r0 * p.D, p.D, stream);
+    st = chunk_grad_inputs<E>(z, ldv, static_cast<int>(ldv), wt, ldv, rows, D, p.chunk,
+                              static_cast<int>(wl.ksplit), dxp, p.grad_x + r0 * p.D, p.D,
+                              mean_count, stream);
     if (st != LMX_OK) return st;
     // 6. grad_weight, once per group of chunks
     if (slot == grp - 1 || c == nchunks - 1) {
@@ -462,28 +491,30 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws_base, hipStream_t stream
       const bool first = gi == 0, last = gi == ngroups - 1;
       int mode;
       if (p.accum == LMX_ACC_F32) {
-        mode = ngroups == 1 ? kDwStoreBf16 : first ? kDwStoreF32 : last ? kDwAddF32ToBf16 : kDwAddF32;
+        mode = ngroups == 1 ? kDwStoreW16 : first ? kDwStoreF32 : last ? kDwAddF32ToW16 : kDwAddF32;
       } else {
-        mode = first ? kDwStoreBf16 : kDwAddBf16;
+        mode = first ? kDwStoreW16 : kDwAddW16;
       }
-      st = grad_weight_product(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw, p.grad_w,
-                               p.D, mode, stream);
+      st = grad_weight_product<E>(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw,
+                                  p.grad_w, p.D, mode, mean_count, stream);
       if (st != LMX_OK) return st;
     }
   }
   return finish_enqueue(row_loss, p.BT, n_ws, p.reduction, p.loss, stream);
 }
 
-int linear_loss_logits_enqueue(const uint16_t* xc, const uint16_t* w, int rows, int D, int V,
-                               uint16_t* logits, int64_t ld_logits, hipStream_t stream) {
+template <typename E>
+int linear_loss_logits_run(const uint16_t* xc, const uint16_t* w, int rows, int D, int V,
+                           uint16_t* logits, int64_t ld_logits, hipStream_t stream) {
   if (rows == 0) return LMX_OK;
   const int tile = pick_tile(rows, V);
   GemmShape g = make_shape(xc, D, w, D, rows, V, V, D, 1, tile);
-  EpiBf16 e{logits, ld_logits, nullptr, 0};
-  return launch_gemm<1>(g, tile, e, stream);
+  EpiOut<E> e{logits, ld_logits, nullptr, 0, nullptr};
+  return launch_gemm<1, E>(g, tile, e, stream);
 }
 
-int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws_base, hipStream_t stream) {
+template <typename E>
+int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t stream) {
   const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum, true);
   char* ws = static_cast<char*>(ws_base);
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
@@ -503,18 +534,35 @@ int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws_base, hipStream
   if (st != LMX_OK) return st;
   st = transpose_pad(p.g, p.ld_g, p.rows, V, gt, ldc, static_cast<int>(ldc), stream);
   if (st != LMX_OK) return st;
-  st = chunk_grad_inputs(p.g, p.ld_g, V, wt, ldv, p.rows, D, p.chunk,
-                         static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, stream);
+  st = chunk_grad_inputs<E>(p.g, p.ld_g, V, wt, ldv, p.rows, D, p.chunk,
+                            static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, nullptr, stream);
   if (st != LMX_OK) return st;
   const bool first = p.index == 0, last = p.index == nchunks - 1;
   int mode;
   if (p.accum == LMX_ACC_F32) {
-    mode = nchunks == 1 ? kDwStoreBf16 : first ? kDwStoreF32 : last ? kDwAddF32ToBf16 : kDwAddF32;
+    mode = nchunks == 1 ? kDwStoreW16 : first ? kDwStoreF32 : last ? kDwAddF32ToW16 : kDwAddF32;
   } else {
-    mode = first ? kDwStoreBf16 : kDwAddBf16;
+    mode = first ? kDwStoreW16 : kDwAddW16;
   }
-  return grad_weight_product(gt, xt, ldc, static_cast<int>(ldc), V, D, dw, p.grad_w, p.D, mode,
-                             stream);
+  return grad_weight_product<E>(gt, xt, ldc, static_cast<int>(ldc), V, D, dw, p.grad_w, p.D, mode,
+                                nullptr, stream);
+}
+
+int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream) {
+  return p.dtype == LMX_F16 ? linear_ce_run<F16>(p, ws, stream)
+                            : linear_ce_run<Bf16>(p, ws, stream);
+}
+
+int linear_loss_logits_enqueue(int dtype, const uint16_t* xc, const uint16_t* w, int rows, int D,
+                               int V, uint16_t* logits, int64_t ld_logits, hipStream_t stream) {
+  return dtype == LMX_F16
+             ? linear_loss_logits_run<F16>(xc, w, rows, D, V, logits, ld_logits, stream)
+             : linear_loss_logits_run<Bf16>(xc, w, rows, D, V, logits, ld_logits, stream);
+}
+
+int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws, hipStream_t stream) {
+  return p.dtype == LMX_F16 ? linear_loss_grads_run<F16>(p, ws, stream)
+                            : linear_loss_grads_run<Bf16>(p, ws, stream);
 }
 
 }  // namespace lmx

@@ -35,7 +35,9 @@ import torch
 
 from lm_head_cross_pass_amd import _lib
 
-_DTYPES = {torch.float32: _lib.LMX_F32, torch.bfloat16: _lib.LMX_BF16}
+_DTYPES = {torch.float32: _lib.LMX_F32, torch.bfloat16: _lib.LMX_BF16,
+           torch.float16: _lib.LMX_F16}
+_LINEAR_DTYPES = {torch.bfloat16: _lib.LMX_BF16, torch.float16: _lib.LMX_F16}
 _REDUCTIONS = {"mean": _lib.LMX_MEAN, "sum": _lib.LMX_SUM}
 _ACCUMS = {"fp32": _lib.LMX_ACC_F32, "weight": _lib.LMX_ACC_WEIGHT}
 
@@ -136,8 +138,10 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
         _require_device(t, n)
         if t.dim() != 2 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous 2-D tensor")
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{n} must be bfloat16 (the matmuls run in bf16)")
+        if t.dtype not in _LINEAR_DTYPES:
+            raise ValueError(f"{n} must be bfloat16 or float16 (the matmuls' input formats)")
+    if inputs.dtype != weight.dtype:
+        raise ValueError("inputs and weight must have the same dtype")
     BT, D = inputs.shape
     V, D2 = weight.shape
     if D2 != D:
@@ -152,7 +156,8 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
         raise ValueError("target must have shape [BT]")
     cs = 0 if chunk_size is None else int(chunk_size)
     acc = _ACCUMS[grad_weight_accum_dtype]
-    nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, _lib.LMX_BF16, cs, acc)
+    ldt = _LINEAR_DTYPES[inputs.dtype]
+    nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, ldt, cs, acc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
@@ -162,7 +167,7 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
     gw = torch.empty_like(weight)
     with torch.cuda.device(dev):
         st = _lib.linear_ce(inputs.data_ptr(), weight.data_ptr(), target.data_ptr(), BT, D, V,
-                            _lib.LMX_BF16, int(ignore_index), _REDUCTIONS[reduction],
+                            ldt, int(ignore_index), _REDUCTIONS[reduction],
                             float(z_loss_multiplier), cs, acc, loss.data_ptr(), gx.data_ptr(),
                             gw.data_ptr(), n_valid.data_ptr(), bad.data_ptr(),
                             workspace.data_ptr(), workspace.numel(), _stream_handle(dev))
@@ -314,14 +319,17 @@ def chunked_linear_loss_fwd(inputs: torch.Tensor, weight: torch.Tensor, loss_and
                             grad_weight_accum_dtype: str = "fp32", workspace=None):
     """One pass: (sum of the chunk losses, grad_inputs, grad_weight) for an upstream
     gradient of 1. The logits chunk handed to ``loss_and_grad_fn`` is a fresh
-    [rows, V] bf16 tensor, which the function may overwrite with its gradient."""
+    [rows, V] tensor in the inputs' dtype (bf16 or fp16), which the function
+    may overwrite with its gradient."""
     loss_kwargs = loss_kwargs or {}
     for t, n in ((inputs, "inputs"), (weight, "weight")):
         _require_device(t, n)
         if t.dim() != 2 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous 2-D tensor")
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{n} must be bfloat16 (the matmuls run in bf16)")
+        if t.dtype not in _LINEAR_DTYPES:
+            raise ValueError(f"{n} must be bfloat16 or float16 (the matmuls' input formats)")
+    if inputs.dtype != weight.dtype:
+        raise ValueError("inputs and weight must have the same dtype")
     BT, D = inputs.shape
     V, D2 = weight.shape
     if D2 != D:
@@ -339,8 +347,9 @@ def chunked_linear_loss_fwd(inputs: torch.Tensor, weight: torch.Tensor, loss_and
     if BT == 0:
         gw.zero_()
         return total, gx, gw
+    ldt = _LINEAR_DTYPES[inputs.dtype]
     C = _lib.linear_ce_chunk_rows(BT, V, cs)
-    nbytes = _lib.linear_loss_workspace_bytes(BT, D, V, _lib.LMX_BF16, cs, acc)
+    nbytes = _lib.linear_loss_workspace_bytes(BT, D, V, ldt, cs, acc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, dev)
     stream = _stream_handle(dev)
@@ -348,20 +357,20 @@ def chunked_linear_loss_fwd(inputs: torch.Tensor, weight: torch.Tensor, loss_and
         for ci, r0 in enumerate(range(0, BT, C)):
             r1 = min(BT, r0 + C)
             rows = r1 - r0
-            logits = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
+            logits = torch.empty((rows, V), dtype=inputs.dtype, device=dev)
             _lib.check("linear_loss_logits", _lib.linear_loss_logits(
-                inputs[r0:r1].data_ptr(), weight.data_ptr(), rows, D, V, _lib.LMX_BF16,
+                inputs[r0:r1].data_ptr(), weight.data_ptr(), rows, D, V, ldt,
                 logits.data_ptr(), V, stream))
             args = [_slice_rows(a, BT, r0, r1) for a in loss_args]
             kwargs = {k: _slice_rows(v, BT, r0, r1) for k, v in loss_kwargs.items()}
             loss_c, g = loss_and_grad_fn(logits, *args, **kwargs)
             if g.shape != (rows, V):
                 raise ValueError("loss_and_grad_fn must return a gradient shaped like the logits")
-            g = g.to(torch.bfloat16).contiguous()
+            g = g.to(inputs.dtype).contiguous()
             total += loss_c.detach().to(torch.float32)
             _lib.check("linear_loss_grads", _lib.linear_loss_grads(
                 inputs[r0:r1].data_ptr(), weight.data_ptr(), g.data_ptr(), V, rows, BT, D, V,
-                _lib.LMX_BF16, cs, acc, ci, gx[r0:r1].data_ptr(), gw.data_ptr(),
+                ldt, cs, acc, ci, gx[r0:r1].data_ptr(), gw.data_ptr(),
                 workspace.data_ptr(), workspace.numel(), stream))
     return total, gx, gw
 

@@ -109,7 +109,7 @@ def _ce(**kw):
     (dict(V=1 << 30), _lib.LMX_ERR_SIZE),
     (dict(V=(1 << 29) - 8), _lib.LMX_ERR_SIZE),          # fp32 row past 2^31 - 64 bytes
     (dict(B=1 << 62), _lib.LMX_ERR_SIZE),
-    (dict(dtype=2), _lib.LMX_ERR_ENUM),
+    (dict(dtype=3), _lib.LMX_ERR_ENUM),
     (dict(red=2), _lib.LMX_ERR_ENUM),
     (dict(logits=A + 2), _lib.LMX_ERR_ALIGN),           # fp32 needs 4-byte alignment
     (dict(target=A + 4), _lib.LMX_ERR_ALIGN),
@@ -189,7 +189,7 @@ def _rows(fn, **kw):
     (dict(B=-1), _lib.LMX_ERR_SIZE),
     (dict(V=0), _lib.LMX_ERR_SIZE),
     (dict(V=1 << 30), _lib.LMX_ERR_SIZE),
-    (dict(dtype=2), _lib.LMX_ERR_ENUM),
+    (dict(dtype=3), _lib.LMX_ERR_ENUM),
     (dict(logits=A + 2), _lib.LMX_ERR_ALIGN),
     (dict(index=A + (2 << 34) + 4), _lib.LMX_ERR_ALIGN),
     (dict(out=A + (3 << 34) + 2), _lib.LMX_ERR_ALIGN),

@@ -5,6 +5,10 @@ Tolerances (stated with the method's workloads):
 * bf16 logits: loss within 2e-3 relative, gradient within 1e-2 relative
   Frobenius norm ||g - g*|| / ||g*||, plus an element-wise bound of one bf16
   rounding on top of the fp32 arithmetic (|g - g*| <= 2^-8 |g*| + 1e-7 scale);
+* fp16 logits: the loss is fp32 arithmetic on exact inputs, so within 1e-5
+  relative as for fp32; the gradient is rounded once to fp16, so within 1e-3
+  relative Frobenius and |g - g*| <= 2^-10 |g*| + 2^-25 + 1e-7 scale element-wise
+  (2^-25 is half the spacing of fp16 subnormals, which the mean's p/N reach);
 * the valid-token count N is compared exactly.
 Inputs are the seeded workloads of ``workloads.py``; the oracle computes on the
 same host bit patterns.
@@ -30,7 +34,7 @@ def _check(logits, target, red, z, got_loss, got_grad, got_n, rows=None, ref=Non
     rl = float(got_loss)
     if math.isnan(ref["loss"]):
         assert math.isnan(rl)
-    elif logits.dtype == torch.float32:
+    elif logits.dtype in (torch.float32, torch.float16):
         assert rl == pytest.approx(ref["loss"], rel=1e-5, abs=1e-30)
     else:
         assert rl == pytest.approx(ref["loss"], rel=2e-3, abs=1e-30)
@@ -43,11 +47,15 @@ def _check(logits, target, red, z, got_loss, got_grad, got_n, rows=None, ref=Non
     if logits.dtype == torch.float32:
         assert float((g - gs).abs().max()) <= 1e-6
     else:
+        fp16 = logits.dtype == torch.float16
         n = float(gs.norm())
         if n > 0:
-            assert float((g - gs).norm()) / n <= 1e-2
+            assert float((g - gs).norm()) / n <= (1e-3 if fp16 else 1e-2)
         scale = 1.0 / max(ref["n_valid"], 1) if red == "mean" else 1.0
-        bound = 2.0 ** -8 * gs.abs() + 1e-7 * scale
+        if fp16:
+            bound = 2.0 ** -10 * gs.abs() + 2.0 ** -25 + 1e-7 * scale
+        else:
+            bound = 2.0 ** -8 * gs.abs() + 1e-7 * scale
         assert bool(((g - gs).abs() <= bound).all()), float(((g - gs).abs() - bound).max())
 
 
@@ -77,6 +85,8 @@ SHAPES = [
     (64, 4097, torch.bfloat16), (130, 1000, torch.float32), (33, 50257, torch.bfloat16),
     (17, 50257, torch.float32), (11, 65536, torch.float32), (4, 131073, torch.bfloat16),
     (6, 70001, torch.float32), (5, 128256, torch.bfloat16),
+    (5, 7, torch.float16), (7, 2041, torch.float16), (9, 2049, torch.float16),
+    (33, 50257, torch.float16), (4, 131073, torch.float16), (5, 128256, torch.float16),
 ]
 
 
@@ -100,16 +110,17 @@ def test_shapes_against_oracle(B, V, dtype):
         assert float(loss3) == pytest.approx(float(loss), rel=2e-6, abs=1e-30)
 
 
-def test_misaligned_rows_and_base():
-    # bf16 rows of odd width, starting 2 bytes past a 16-byte boundary
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_misaligned_rows_and_base(dtype):
+    # 16-bit rows of odd width, starting 2 bytes past a 16-byte boundary
     B, V = 12, 50257
-    logits, target = workloads.small_ce(B + 1, V, dtype=torch.bfloat16, sigma=3.0, n_ignored=2,
+    logits, target = workloads.small_ce(B + 1, V, dtype=dtype, sigma=3.0, n_ignored=2,
                                         seed=3)
     full = logits.to(DEV)
     view = full.view(-1)[1:1 + B * V].view(B, V)           # base offset of one element
     t = target[:B].to(DEV)
     ref_logits = full.view(-1)[1:1 + B * V].view(B, V).cpu()
-    grad = torch.empty((B * V + 8,), dtype=torch.bfloat16, device=DEV)[1:1 + B * V].view(B, V)
+    grad = torch.empty((B * V + 8,), dtype=dtype, device=DEV)[1:1 + B * V].view(B, V)
     loss, g, n, bad = F.ce_fwd_bwd(view, t, -100, "mean", 1e-4, grad=grad)
     _check(ref_logits, target[:B], "mean", 1e-4, loss, g, n)
     before = full.clone()
@@ -163,12 +174,12 @@ def test_extreme_logits():
     x[2, ::2] = -float("inf")          # half the row impossible
     x[3] = torch.linspace(-80, 80, V)
     t = torch.tensor([3, 10, 1, 4999])
-    for dtype in (torch.float32, torch.bfloat16):
+    for dtype in (torch.float32, torch.bfloat16, torch.float16):
         xl = x.to(dtype)
         loss, grad, n, bad, _ = _run(xl, t, "sum", 0.0)
         ref = oracle.cross_entropy(xl, t, -100, "sum", 0.0)
         assert math.isfinite(float(loss))
-        tol = 1e-5 if dtype == torch.float32 else 2e-3
+        tol = 2e-3 if dtype == torch.bfloat16 else 1e-5
         assert float(loss) == pytest.approx(ref["loss"], rel=tol)
         assert bool(torch.isfinite(grad).all())
         assert bool((grad[2, ::2] == 0).all())

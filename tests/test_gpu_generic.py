@@ -6,8 +6,9 @@ The loss-and-gradient functions are the caller's: a sum-of-squares loss through
 cross-entropy the same way, and the library's own cross-entropy
 (``cross_entropy_loss_and_grad``). The logits are bf16 (the matmuls' dtype), so
 the bars are those of the bf16 linear path: loss within 5e-3 relative (2e-3 for
-cross-entropy), each gradient within 1e-2 relative Frobenius norm. Y (the
-regression targets) and the other inputs come from the seeded generators.
+cross-entropy), each gradient within 1e-2 relative Frobenius norm; the same
+bars hold for fp16 logits, whose rounding is finer. Y (the regression targets)
+and the other inputs come from the seeded generators.
 """
 import pytest
 import torch
@@ -35,8 +36,9 @@ def _mse(z, y):
 @pytest.mark.parametrize("BT,D,V,chunk", [(96, 64, 512, 32), (100, 72, 336, 37),
                                           (257, 128, 4096, 100), (64, 64, 1000, 0)])
 @pytest.mark.parametrize("accum", ("fp32", "weight"))
-def test_sum_of_squares_loss(BT, D, V, chunk, accum):
-    X, W, _ = workloads.small_linear_ce(BT, D, V, seed=BT + V, sigma_w=0.1)
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_sum_of_squares_loss(BT, D, V, chunk, accum, dtype):
+    X, W, _ = workloads.small_linear_ce(BT, D, V, dtype=dtype, seed=BT + V, sigma_w=0.1)
     Y = workloads.row_upstream(BT * V, seed=V).reshape(BT, V) * 0.5
     loss, gx, gw = F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV),
                                              F.autograd_loss_and_logits_grad(_mse), (Y.to(DEV),),
@@ -50,9 +52,10 @@ def test_sum_of_squares_loss(BT, D, V, chunk, accum):
 
 
 @pytest.mark.parametrize("how", ("library", "torch"))
-def test_cross_entropy_through_the_generic_path(how):
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_cross_entropy_through_the_generic_path(how, dtype):
     BT, D, V = 300, 96, 2048
-    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=15, seed=9)
+    X, W, t = workloads.small_linear_ce(BT, D, V, dtype=dtype, n_ignored=15, seed=9)
     if how == "library":
         fn = F.cross_entropy_loss_and_grad
     else:

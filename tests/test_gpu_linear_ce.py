@@ -6,6 +6,18 @@ N exact. 'weight' accumulation is compared with the oracle's chunk-by-chunk
 bf16 emulation at the same tolerance. The GPU path rounds the logits and the
 logits gradient to bf16 between its matmuls (the matmuls run in bf16); the
 oracle models no intermediate rounding, and the tolerance covers it.
+
+fp16 inputs (the same path with fp16 matmuls): loss within 5e-4 relative and
+gradients within 2e-3 relative Frobenius (fp16 keeps 3 more significand bits
+than bf16; the emulated error of the two roundings is about 2e-4 on these
+workloads). The mean's 1/N is applied to the fp32 products, never to the fp16
+logits gradient, so probabilities p/N below fp16's smallest subnormal do not
+vanish: ``test_fp16_mean_over_a_large_batch`` is the case where they would.
+The fp16 outputs themselves are gradients of a mean over thousands of tokens,
+often below 2^-14, where fp16 holds only subnormals with a fixed spacing of
+2^-24; the output's own rounding (the oracle's value rounded to fp16) is
+therefore added to the fp16 gradient bar:
+||got - ref|| <= tol ||ref|| + ||fp16(ref) - ref||.
 """
 import math
 
@@ -26,6 +38,20 @@ def _rel(a, b):
     n = float(b.norm())
     d = float((a.double().cpu() - b).norm())
     return d / n if n > 0 else d
+
+
+TOL = {torch.bfloat16: (2e-3, 1e-2), torch.float16: (5e-4, 2e-3)}   # loss rel, grad rel
+
+
+def _grad_ok(got, ref, dtype):
+    """The gradient bar: relative Frobenius error, plus for fp16 outputs the
+    error of rounding the exact value to fp16 itself."""
+    ref = ref.double()
+    d = float((got.double().cpu() - ref).norm())
+    allow = TOL[dtype][1] * float(ref.norm())
+    if dtype == torch.float16:
+        allow += float((oracle.round_to_fp16(ref) - ref).norm())
+    return d <= allow
 
 
 def _run(X, W, t, red, z, chunk, accum="fp32"):
@@ -171,10 +197,16 @@ def test_grouped_grad_weight_products_sampled():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("accum", ("fp32", "weight"))
-def test_workload_bt16384_d4096_v128256_sampled(accum):
+@pytest.mark.parametrize("accum,dtype", (("fp32", torch.bfloat16), ("weight", torch.bfloat16),
+                                         ("fp32", torch.float16)))
+def test_workload_bt16384_d4096_v128256_sampled(accum, dtype):
+    # fp16: the same seeded values converted (every bf16 value of these
+    # magnitudes is an fp16 value or rounds to the nearest fp16 subnormal);
+    # mean over N = 16056 is where scaling G itself would underflow in fp16
     w = workloads.LCE_BT16384_D4096_V128256
     X, W, t = workloads.linear_ce_inputs(w)
+    X, W = X.to(dtype), W.to(dtype)
+    lt, gt = TOL[dtype]
     loss, gx, gw, n, bad = _run(X, W, t, w.reduction, w.z_loss, w.chunk_size, accum)
     assert int(n) == 16056 and int(bad) == 0
     g = torch.Generator().manual_seed(2)
@@ -182,6 +214,71 @@ def test_workload_bt16384_d4096_v128256_sampled(accum):
     vrows = torch.randperm(w.V, generator=g)[:24].tolist() + [int(t[rows[0]])]
     ref = olce.linear_cross_entropy_sampled(X, W, t, rows, vrows, -100, w.reduction, w.z_loss,
                                             block_rows=1024)
-    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
-    assert _rel(gx.cpu()[rows], ref["grad_inputs_rows"]) <= 1e-2
-    assert _rel(gw.cpu()[vrows], ref["grad_weight_rows"]) <= 1e-2
+    assert float(loss) == pytest.approx(ref["loss"], rel=lt)
+    assert _grad_ok(gx.cpu()[rows], ref["grad_inputs_rows"], dtype)
+    assert _grad_ok(gw.cpu()[vrows], ref["grad_weight_rows"], dtype)
+
+
+@pytest.mark.parametrize("BT,D,V,chunk", CASES)
+def test_fp16_shapes_against_oracle(BT, D, V, chunk):
+    X, W, t = workloads.small_linear_ce(BT, D, V, dtype=torch.float16,
+                                        n_ignored=max(1, BT // 20), seed=BT + V)
+    lt, gt = TOL[torch.float16]
+    for red, z in (("mean", 1e-4), ("sum", 0.0), ("mean", 0.5)):
+        ref = oracle.linear_cross_entropy(X, W, t, -100, red, z)
+        loss, gx, gw, n, bad = _run(X, W, t, red, z, chunk)
+        assert gx.dtype == torch.float16 and gw.dtype == torch.float16
+        assert int(n) == ref["n_valid"] and int(bad) == 0
+        assert float(loss) == pytest.approx(ref["loss"], rel=lt)
+        assert _grad_ok(gx, ref["grad_inputs"], torch.float16)
+        assert _grad_ok(gw, ref["grad_weight"], torch.float16)
+        ign = (t == -100).nonzero().flatten()
+        assert bool((gx[ign.to(DEV)] == 0).all())
+
+
+def test_fp16_weight_accumulation_follows_the_chunked_rounding():
+    X, W, t = workloads.small_linear_ce(512, 64, 300, dtype=torch.float16, n_ignored=10, seed=6)
+    chunk = 16
+    lt, gt = TOL[torch.float16]
+    emu = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0, "weight", chunk_size=chunk)
+    exact = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0)
+    loss, gx, gw, n, _ = _run(X, W, t, "sum", 0.0, chunk, "weight")
+    assert float(loss) == pytest.approx(exact["loss"], rel=lt)
+    assert _grad_ok(gw, emu["grad_weight"], torch.float16)
+    assert _grad_ok(gx, exact["grad_inputs"], torch.float16)
+    d_emu = float((gw.double().cpu() - emu["grad_weight"]).norm())
+    d_exact = float((gw.double().cpu() - exact["grad_weight"]).norm())
+    assert d_emu < d_exact
+
+
+@pytest.mark.parametrize("z", (1e-4, 0.5))
+def test_fp16_mean_over_a_large_batch(z):
+    # N = 1946 valid rows over V = 32000: the mean's p/N is about 1.6e-8, under
+    # fp16's smallest subnormal 2^-24; scaling G itself would lose the softmax
+    # part of every gradient row (an error of 2e-2 to 1e-1 here)
+    BT, D, V = 2048, 64, 32000
+    X, W, t = workloads.small_linear_ce(BT, D, V, dtype=torch.float16, n_ignored=102, seed=21)
+    lt, gt = TOL[torch.float16]
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", z, block_rows=512)
+    for accum in ("fp32", "weight"):
+        loss, gx, gw, n, bad = _run(X, W, t, "mean", z, 512, accum)
+        assert int(n) == BT - 102 == ref["n_valid"]
+        assert float(loss) == pytest.approx(ref["loss"], rel=lt)
+        assert _grad_ok(gx, ref["grad_inputs"], torch.float16)
+        assert _grad_ok(gw, ref["grad_weight"], torch.float16)
+
+
+def test_fp16_autograd_wrapper_and_dtype_checks():
+    from lm_head_cross_pass_amd import linear_cross_entropy
+    X, W, t = workloads.small_linear_ce(64, 64, 500, dtype=torch.float16, n_ignored=3, seed=7)
+    Xd = X.to(DEV).requires_grad_(True)
+    Wd = W.to(DEV).requires_grad_(True)
+    loss = linear_cross_entropy(Xd, Wd, t.to(DEV), -100, "mean", 1e-4, chunk_size=16)
+    (3.0 * loss).backward()
+    lt, gt = TOL[torch.float16]
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4)
+    assert float(loss.detach()) == pytest.approx(ref["loss"], rel=lt)
+    assert _grad_ok(Xd.grad, 3.0 * ref["grad_inputs"], torch.float16)
+    assert _grad_ok(Wd.grad, 3.0 * ref["grad_weight"], torch.float16)
+    with pytest.raises(ValueError):   # inputs and weight in different formats
+        F.linear_ce(X.to(DEV), W.to(DEV).bfloat16(), t.to(DEV), -100, "mean", 0.0, 16)

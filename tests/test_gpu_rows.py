@@ -9,6 +9,9 @@ Tolerances:
   (the reduced path's 1e-6 absolute bar, scaled by the row's upstream
   gradient); bf16 logits: relative Frobenius error <= 1e-2 and element-wise
   one bf16 rounding on top of fp32 arithmetic (2^-8 |ref| + 1e-7 |g_i|);
+  fp16 logits: the same with the fp16 unit roundoff, relative Frobenius error
+  <= 1e-3 and element-wise 2^-10 |ref| + 2^-25 + 1e-7 |g_i| (2^-25 is half the
+  spacing of fp16 subnormals, where the smallest probabilities land);
 * ignored rows exactly 0; N and the out-of-range flag exactly.
 The VJP's loss input is the oracle's per-row loss rounded to fp32 (never a GPU
 value); g comes from the seeded ``workloads.row_upstream``.
@@ -27,6 +30,8 @@ SHAPES = [
     (3, 1, torch.float32), (5, 7, torch.bfloat16), (9, 2049, torch.bfloat16),
     (130, 1000, torch.float32), (33, 50257, torch.bfloat16), (17, 50257, torch.float32),
     (4, 131073, torch.bfloat16), (6, 70001, torch.float32), (5, 128256, torch.bfloat16),
+    (5, 7, torch.float16), (9, 2049, torch.float16), (33, 50257, torch.float16),
+    (5, 128256, torch.float16),
 ]
 
 
@@ -43,10 +48,14 @@ def _vjp_close(got, ref, g, dtype):
         bound = 1e-6 * torch.clamp(gi, min=1.0)
         assert bool(((got - ref).abs() <= bound).all()), float(((got - ref).abs() - bound).max())
     else:
+        fp16 = dtype == torch.float16
         n = float(ref.norm())
         if n > 0:
-            assert float((got - ref).norm()) / n <= 1e-2
-        bound = 2.0 ** -8 * ref.abs() + 1e-7 * gi
+            assert float((got - ref).norm()) / n <= (1e-3 if fp16 else 1e-2)
+        if fp16:
+            bound = 2.0 ** -10 * ref.abs() + 2.0 ** -25 + 1e-7 * gi
+        else:
+            bound = 2.0 ** -8 * ref.abs() + 1e-7 * gi
         assert bool(((got - ref).abs() <= bound).all()), float(((got - ref).abs() - bound).max())
 
 
