@@ -20,10 +20,11 @@ dense bf16 MFMA peak), plus its 'weight'-accumulation variant timed on its own.
 reduced CE, selective_log_softmax, the unreduced per-row CE and its VJP), each
 in GB/s of its own algorithmic bytes; ``linear_ce.generic_chunked_loss`` times the
 generic chunked linear loss with the library's cross-entropy as the caller's loss
-on the linear-CE inputs. ``cpu_baseline`` is the fp64 oracle timed
+on the linear-CE inputs; ``fp16`` times the CE and the fused linear-CE on the
+same values converted to IEEE binary16. ``cpu_baseline`` is the fp64 oracle timed
 on the host on a bounded sample of the same CE workload.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows,generic] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows,generic,fp16] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -83,9 +84,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="ce,linear,rows,generic",
+    ap.add_argument("--legs", default="ce,linear,rows,generic,fp16",
                     help="ce, linear, rows (per-row entry points; needs ce), generic (the "
-                         "generic chunked linear loss; needs linear)")
+                         "generic chunked linear loss; needs linear), fp16 (the ce and linear "
+                         "legs' workloads in fp16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--weight-steps", type=int, default=3)
     args = ap.parse_args()
@@ -336,6 +338,67 @@ def main() -> int:
                                "algorithmic_bytes": nbytes, "frac": round(gbps / HBM_PEAK_GBPS, 4)}
             log(f"{name}: {ms:.3f} ms, {gbps:.0f} GB/s")
         line["next_rows"] = rows_line
+
+    # ------------------------------------------------------------ fp16 inputs
+    # the same workloads with the values converted to IEEE binary16: the CE row
+    # kernel (out of place) and the fused linear-CE with fp16 matmuls
+    if "fp16" in legs:
+        f16 = {}
+        if "ce" in legs:
+            B, V = ce_w.B, ce_w.V
+            x16 = copies[0].to(torch.float16)
+            g16 = torch.empty_like(x16)
+
+            def ce16():
+                _lib.check("ce_fwd_bwd", _lib.ce_fwd_bwd(
+                    x16.data_ptr(), g16.data_ptr(), target.data_ptr(), B, V, _lib.LMX_F16, -100,
+                    _lib.LMX_SUM, 0.0, ce_out[0].data_ptr(), ce_out[1].data_ptr(),
+                    ce_out[2].data_ptr(), ce_ws.data_ptr(), ce_ws.numel(), stream.cuda_stream))
+            for _ in range(3):
+                ce16()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(10):
+                ce16()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            nbytes = 2 * B * V * 2 + 8 * B
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            f16["ce_fwd_bwd"] = {"value": round(gbps, 1), "unit": "GB/s", "ms_per_call": round(ms, 4),
+                                 "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                                 "workload": ce_w.name + " as fp16, out of place"}
+            log(f"fp16 CE: {ms:.3f} ms, {gbps:.0f} GB/s")
+            del x16, g16
+        if "linear" in legs:
+            X16, W16 = X.to(torch.float16), Wt.to(torch.float16)
+            gx16, gw16 = torch.empty_like(X16), torch.empty_like(W16)
+
+            def lin16():
+                _lib.check("linear_ce", _lib.linear_ce(
+                    X16.data_ptr(), W16.data_ptr(), tl.data_ptr(), lin_w.BT, lin_w.D, lin_w.V,
+                    _lib.LMX_F16, -100, _lib.LMX_MEAN, lin_w.z_loss, lin_w.chunk_size,
+                    _lib.LMX_ACC_F32, lin_out[0].data_ptr(), gx16.data_ptr(), gw16.data_ptr(),
+                    lin_out[1].data_ptr(), lin_out[2].data_ptr(), lin_ws.data_ptr(),
+                    lin_ws.numel(), stream.cuda_stream))
+            lin16()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(3):
+                lin16()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 3
+            flops = 6.0 * lin_w.BT * lin_w.V * lin_w.D
+            tf = flops / (ms * 1e-3) / 1e12
+            f16["linear_ce"] = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(ms, 3),
+                                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "workload": lin_w.name + " as fp16, fp32 accumulation"}
+            log(f"fp16 linear-CE: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+            del X16, W16, gx16, gw16
+        line["fp16"] = f16
 
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu and "ce" in legs:
