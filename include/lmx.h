@@ -210,7 +210,9 @@ LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t
  *   grad_inputs[chunk rows] = G_c @ weight,
  *   grad_weight            (+)= G_c^T @ inputs_c,
  * accumulated over the chunks in fp32 (LMX_ACC_F32: a workspace accumulator,
- * rounded to the 16-bit format once, by the last chunk's call) or in grad_weight itself
+ * rounded to the 16-bit format once, by the last chunk's call; the product is
+ * taken once per group of chunks whose G_c^T the workspace holds together,
+ * so some calls only store their chunk's operands) or in grad_weight itself
  * (LMX_ACC_WEIGHT: rounded after every chunk), the page's
  * grad_weight_accum_dtype.
  *

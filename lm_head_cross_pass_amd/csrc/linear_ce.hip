@@ -386,8 +386,9 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   // fp32 accumulation takes the grad_weight product of several chunks at once
   // (K = group ldc): as many chunks as G^T of 1 GiB holds, so the fp32
   // accumulator is read and written once per group instead of once per chunk
+  // (in the fused and the generic path alike)
   w.dw_group = 1;
-  if (accum == LMX_ACC_F32 && nchunks > 1 && !generic) {
+  if (accum == LMX_ACC_F32 && nchunks > 1) {
     const int64_t per_chunk = w.ldv * w.ldc * 2;
     int64_t gsz = (int64_t{1} << 30) / per_chunk;
     if (gsz > nchunks) gsz = nchunks;
@@ -523,29 +524,34 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
   const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
-  const int64_t ldv = wl.ldv, ldc = wl.ldc;
+  const int64_t ldv = wl.ldv, ldc = wl.ldc, ldk = wl.ldk, grp = wl.dw_group;
   const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
+  const int64_t slot = p.index % grp;   // this chunk's columns in G^T and X^T
   int st;
   if (p.index == 0) {   // W^T for every chunk of the pass
     st = transpose_pad(p.w, p.D, V, D, wt, ldv, static_cast<int>(ldv), stream);
     if (st != LMX_OK) return st;
   }
-  st = transpose_pad(p.xc, p.D, p.rows, D, xt, ldc, static_cast<int>(ldc), stream);
+  st = transpose_pad(p.xc, p.D, p.rows, D, xt + slot * ldc, ldk, static_cast<int>(ldc), stream);
   if (st != LMX_OK) return st;
-  st = transpose_pad(p.g, p.ld_g, p.rows, V, gt, ldc, static_cast<int>(ldc), stream);
+  st = transpose_pad(p.g, p.ld_g, p.rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
   if (st != LMX_OK) return st;
   st = chunk_grad_inputs<E>(p.g, p.ld_g, V, wt, ldv, p.rows, D, p.chunk,
                             static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, nullptr, stream);
   if (st != LMX_OK) return st;
-  const bool first = p.index == 0, last = p.index == nchunks - 1;
+  // grad_weight, once per group of chunks (the group's G^T and X^T columns
+  // stay in the workspace between the calls)
+  if (slot != grp - 1 && p.index != nchunks - 1) return LMX_OK;
+  const int64_t gi = p.index / grp, ngroups = (nchunks + grp - 1) / grp;
+  const bool first = gi == 0, last = gi == ngroups - 1;
   int mode;
   if (p.accum == LMX_ACC_F32) {
-    mode = nchunks == 1 ? kDwStoreW16 : first ? kDwStoreF32 : last ? kDwAddF32ToW16 : kDwAddF32;
+    mode = ngroups == 1 ? kDwStoreW16 : first ? kDwStoreF32 : last ? kDwAddF32ToW16 : kDwAddF32;
   } else {
     mode = first ? kDwStoreW16 : kDwAddW16;
   }
-  return grad_weight_product<E>(gt, xt, ldc, static_cast<int>(ldc), V, D, dw, p.grad_w, p.D, mode,
-                                nullptr, stream);
+  return grad_weight_product<E>(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw,
+                                p.grad_w, p.D, mode, nullptr, stream);
 }
 
 int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream) {

@@ -106,3 +106,30 @@ def test_vocabulary_must_give_16_byte_gradient_rows():
     with pytest.raises(ValueError):
         F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV), F.cross_entropy_loss_and_grad,
                                   (torch.zeros(32, dtype=torch.int64, device=DEV),))
+
+
+def test_grouped_grad_weight_products_generic():
+    """Five chunks of 2048 rows at V = 128256 through the generic path: fp32
+    accumulation takes the grad_weight product once per pair of chunks (the
+    pair's G^T columns wait in the workspace between calls), then the last
+    chunk alone; checked against the oracle on sampled rows and against the
+    fused linear_ce on everything."""
+    from oracle import linear_ce as olce
+    BT, D, V, C = 5 * 2048, 64, 128256, 2048
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=200, seed=13)
+    Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
+    loss, gx, gw = F.chunked_linear_loss_fwd(Xd, Wd, F.cross_entropy_loss_and_grad, (td,),
+                                             chunk_size=C)
+    loss_f, gx_f, gw_f, _, _ = F.linear_ce(Xd, Wd, td, -100, "sum", 0.0, C, "fp32")
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(5)
+    rows = torch.randperm(BT, generator=g)[:16].tolist()
+    vrows = torch.randperm(V, generator=g)[:16].tolist() + [int(t[rows[0]]), V - 1]
+    ref = olce.linear_cross_entropy_sampled(X, W, t, rows, vrows, -100, "sum", 0.0,
+                                            block_rows=1024)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx.cpu()[rows], ref["grad_inputs_rows"]) <= 1e-2
+    assert _rel(gw.cpu()[vrows], ref["grad_weight_rows"]) <= 1e-2
+    assert float(loss) == pytest.approx(float(loss_f), rel=1e-5)
+    assert _rel(gx, gx_f.double().cpu()) <= 1e-2
+    assert _rel(gw, gw_f.double().cpu()) <= 1e-2
