@@ -313,6 +313,27 @@ LMX_API int ce_loss_rows_vjp(const void* logits, const int64_t* target, const fl
                              const float* g, void* grad_logits, int64_t B, int64_t V, int dtype,
                              int64_t ignore_index, void* stream);
 
+/*
+ * lmx_scale -- dst[i] = src[i] * (*scale), in fp32 arithmetic, rounded to
+ * nearest even into `dtype` (LMX_F32, LMX_BF16 or LMX_F16).
+ *
+ * The upstream-gradient step of the reduced losses (greyhound functional API
+ * page, "cross_entropy", "chunked_linear_cross_entropy" and
+ * "chunked_linear_loss": normal autograd behaviour): the entry points above
+ * return the gradients for an upstream gradient of 1, and an autograd backward
+ * multiplies them by the upstream scalar. Taking the product in fp32 keeps a
+ * large fp16 loss scale (2^16 and more) from overflowing and a scale such as
+ * 1/3 from being rounded to 16 bits first.
+ *
+ *   src, dst   n elements of `dtype`, element-aligned (16-byte alignment of
+ *              both takes the vector path); dst may be exactly src (in
+ *              place); any other overlap is LMX_ERR_ALIAS.
+ *   n          >= 0 (0 launches nothing; < 0 is LMX_ERR_SIZE).
+ *   scale      one fp32 on the device, 4-byte aligned, not inside dst.
+ */
+LMX_API int lmx_scale(const void* src, void* dst, int64_t n, int dtype, const float* scale,
+                      void* stream);
+
 /* Human-readable name of a status code (static storage). */
 LMX_API const char* lmx_status_string(int status);
 

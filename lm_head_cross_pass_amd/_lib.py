@@ -41,6 +41,7 @@ _SIGNATURES = {
     "linear_ce_chunk_rows": (_i64, [_i64, _i64, _i64]),
     "lmx_status_string": (ctypes.c_char_p, [_i32]),
     "lmx_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "lmx_scale": (_i32, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "selective_log_softmax": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "ce_loss_rows": (_i32, [_vp, _vp, _i64, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ce_loss_rows_vjp": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp]),
@@ -124,6 +125,10 @@ def linear_ce_chunk_rows(BT, V, chunk_size) -> int:
 
 def lmx_copy(src, dst, nbytes, stream) -> int:
     return load().lmx_copy(src, dst, nbytes, stream)
+
+
+def lmx_scale(src, dst, n, dtype, scale, stream) -> int:
+    return load().lmx_scale(src, dst, n, dtype, scale, stream)
 
 
 def selective_log_softmax(logits, index, B, V, dtype, out, bad_index, workspace,

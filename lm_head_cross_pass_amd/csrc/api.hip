@@ -364,6 +364,23 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
   return lmx::linear_ce_enqueue(p, workspace, static_cast<hipStream_t>(stream));
 }
 
+int lmx_scale(const void* src, void* dst, int64_t n, int dtype, const float* scale,
+              void* stream) {
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
+  if (n < 0) return LMX_ERR_SIZE;
+  if (n == 0) return LMX_OK;
+  if (src == nullptr || dst == nullptr || scale == nullptr) return LMX_ERR_NULL;
+  const size_t es = dtype == LMX_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(src) % es != 0 || reinterpret_cast<uintptr_t>(dst) % es != 0 ||
+      reinterpret_cast<uintptr_t>(scale) % 4 != 0)
+    return LMX_ERR_ALIGN;
+  if (static_cast<uint64_t>(n) > (UINT64_MAX / 2) / es) return LMX_ERR_SIZE;
+  const size_t bytes = static_cast<size_t>(n) * es;
+  if (src != dst && overlaps(src, bytes, dst, bytes)) return LMX_ERR_ALIAS;
+  if (overlaps(scale, 4, dst, bytes)) return LMX_ERR_ALIAS;
+  return lmx::scale_enqueue(src, dst, n, dtype, scale, static_cast<hipStream_t>(stream));
+}
+
 int lmx_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return LMX_OK;
   if (src == nullptr || dst == nullptr) return LMX_ERR_NULL;

@@ -114,4 +114,8 @@ int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws, hipStream_t st
 
 int copy_enqueue(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
+// dst[i] = RNE(src[i] * (*scale)) in fp32 arithmetic, for n elements of dtype.
+int scale_enqueue(const void* src, void* dst, int64_t n, int dtype, const float* scale,
+                  hipStream_t stream);
+
 }  // namespace lmx

@@ -56,6 +56,21 @@ def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _scaled(t: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
+    """``t * g`` for the upstream scalar gradient ``g`` of a reduced loss: a new
+    tensor, the product taken in fp32 by the library (so a large fp16 loss scale
+    does not overflow and ``g`` is not first rounded to 16 bits)."""
+    out = torch.empty_like(t)
+    if t.numel() == 0:
+        return out
+    s = g.detach().to(device=t.device, dtype=torch.float32).reshape(()).contiguous()
+    with torch.cuda.device(t.device):
+        st = _lib.lmx_scale(t.data_ptr(), out.data_ptr(), t.numel(), _DTYPES[t.dtype],
+                            s.data_ptr(), _stream_handle(t.device))
+    _lib.check("lmx_scale", st)
+    return out
+
+
 def ce_fwd_bwd(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
                reduction: str = "mean", z_loss_multiplier: float = 0.0,
                grad: Optional[torch.Tensor] = None, want_grad: bool = True,
@@ -111,7 +126,7 @@ class _CrossEntropy(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         (grad,) = ctx.saved_tensors
-        return grad * grad_out.to(grad.dtype), None, None, None, None
+        return _scaled(grad, grad_out), None, None, None, None
 
 
 def cross_entropy(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
@@ -186,8 +201,7 @@ class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         gx, gw = ctx.saved_tensors
-        g = grad_out.to(gx.dtype)
-        return gx * g, gw * g, None, None, None, None, None, None
+        return _scaled(gx, grad_out), _scaled(gw, grad_out), None, None, None, None, None, None
 
 
 def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
@@ -386,8 +400,7 @@ class _ChunkedLinearLoss(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         gx, gw = ctx.saved_tensors
-        g = grad_out.to(gx.dtype)
-        return gx * g, gw * g, None, None, None, None, None
+        return _scaled(gx, grad_out), _scaled(gw, grad_out), None, None, None, None, None
 
 
 def chunked_linear_loss(inputs: torch.Tensor, weight: torch.Tensor, loss_and_grad_fn,

@@ -30,7 +30,8 @@ def test_every_declared_function_is_exported():
     names = _lib.header_functions()
     assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "linear_ce",
                           "linear_ce_workspace_bytes", "linear_ce_chunk_rows",
-                          "lmx_status_string", "lmx_copy", "selective_log_softmax",
+                          "lmx_status_string", "lmx_copy", "lmx_scale",
+                          "selective_log_softmax",
                           "ce_loss_rows", "ce_loss_rows_vjp", "linear_loss_logits",
                           "linear_loss_grads", "linear_loss_workspace_bytes"}
     lib = _lib.load()
@@ -159,6 +160,20 @@ def _lin(**kw):
 ])
 def test_linear_ce_argument_errors(kw, status):
     assert _lin(**kw) == status
+
+
+def test_scale_argument_errors():
+    S = A + (5 << 34)
+    assert _lib.lmx_scale(A, A, 8, 3, S, None) == _lib.LMX_ERR_ENUM
+    assert _lib.lmx_scale(A, A, -1, F32, S, None) == _lib.LMX_ERR_SIZE
+    assert _lib.lmx_scale(A, A, 0, F32, None, None) == _lib.LMX_OK      # nothing to do
+    assert _lib.lmx_scale(None, A, 8, F32, S, None) == _lib.LMX_ERR_NULL
+    assert _lib.lmx_scale(A, A, 8, F32, None, None) == _lib.LMX_ERR_NULL
+    assert _lib.lmx_scale(A + 2, A + (1 << 34), 8, F32, S, None) == _lib.LMX_ERR_ALIGN
+    assert _lib.lmx_scale(A + 1, A + (1 << 34), 8, _lib.LMX_BF16, S, None) == _lib.LMX_ERR_ALIGN
+    assert _lib.lmx_scale(A, A, 8, F32, S + 2, None) == _lib.LMX_ERR_ALIGN
+    assert _lib.lmx_scale(A, A + 16, 8, F32, S, None) == _lib.LMX_ERR_ALIAS   # partial overlap
+    assert _lib.lmx_scale(A, A + (1 << 34), 8, F32, A + (1 << 34) + 4, None) == _lib.LMX_ERR_ALIAS
 
 
 def test_copy_argument_errors():
