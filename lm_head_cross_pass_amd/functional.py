@@ -9,15 +9,16 @@ computation runs in the library's kernels. The functions:
   logits with their gradient (upstream gradient 1);
 * ``linear_cross_entropy`` -- chunked ``inputs @ weight.T`` cross-entropy with
   gradients for inputs and weight (page entries ``chunked_linear_loss`` and
-  ``chunked_linear_cross_entropy``; ``chunk_size`` as in the former);
+  ``chunked_linear_cross_entropy``; ``chunk_size`` as in the former), and
+  ``chunked_linear_cross_entropy`` with that entry's own signature;
 * ``chunked_linear_loss`` with ``autograd_loss_and_logits_grad`` -- the
   generic chunked linear loss: the library computes each chunk's logits and,
   from the caller's logits gradient, the chunk's grad_inputs rows and its
   share of grad_weight (page entries ``chunked_linear_loss`` and
   ``autograd_loss_and_logits_grad``); ``cross_entropy_loss_and_grad`` is the
   library's cross-entropy in that loss-and-gradient form;
-* ``selective_log_softmax`` -- one log-probability per row (page entry
-  ``selective_log_softmax``);
+* ``selective_log_softmax`` -- one log-probability per row of ``[..., V]``
+  logits (page entry ``selective_log_softmax``);
 * ``cross_entropy_per_row`` -- the unreduced per-row cross-entropy whose
   backward is the separate vector-Jacobian product call (nuvec ``FastOp``
   page, ``CrossEntropy`` / ``CrossEntropyVjp``).
@@ -213,6 +214,18 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
                                      z_loss_multiplier, chunk_size, grad_weight_accum_dtype)
 
 
+def chunked_linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                                 ignore_index: int = -100, reduction: str = "mean",
+                                 z_loss_multiplier: float = 0.0,
+                                 grad_weight_accum_dtype: str = "fp32", *,
+                                 chunk_size: Optional[int] = None) -> torch.Tensor:
+    """The page's ``chunked_linear_cross_entropy``, argument for argument (the
+    row-chunk size, which that entry leaves to the library, may be given by
+    keyword); the same computation as ``linear_cross_entropy``."""
+    return _LinearCrossEntropy.apply(inputs, weight, target, ignore_index, reduction,
+                                     z_loss_multiplier, chunk_size, grad_weight_accum_dtype)
+
+
 def _rows_args(logits: torch.Tensor, index: torch.Tensor, what: str):
     _require_device(logits, "logits")
     if logits.dim() != 2 or not logits.is_contiguous():
@@ -227,7 +240,18 @@ def _rows_args(logits: torch.Tensor, index: torch.Tensor, what: str):
 
 
 def selective_log_softmax(logits: torch.Tensor, index: torch.Tensor) -> torch.Tensor:
-    """``log_softmax(logits, -1).gather(-1, index[:, None])[:, 0]`` as fp32 [B]; no autograd."""
+    """``log_softmax(logits, -1).gather(-1, index[..., None])[..., 0]`` in fp32; no autograd.
+
+    ``logits`` is ``[..., V]`` (contiguous) and ``index`` has its leading shape
+    ``[...]``; the result has that shape too."""
+    if logits.dim() != 2:
+        if logits.dim() < 1 or not logits.is_contiguous():
+            raise ValueError("logits must be a contiguous [..., V] tensor")
+        lead = logits.shape[:-1]
+        if tuple(index.shape) != tuple(lead):
+            raise ValueError("index must have the leading shape of logits")
+        return selective_log_softmax(logits.reshape(-1, logits.shape[-1]),
+                                     index.reshape(-1)).reshape(lead)
     B, V, index = _rows_args(logits, index, "index")
     dev = logits.device
     out = torch.empty(B, dtype=torch.float32, device=dev)

@@ -282,3 +282,26 @@ def test_fp16_autograd_wrapper_and_dtype_checks():
     assert _grad_ok(Wd.grad, 3.0 * ref["grad_weight"], torch.float16)
     with pytest.raises(ValueError):   # inputs and weight in different formats
         F.linear_ce(X.to(DEV), W.to(DEV).bfloat16(), t.to(DEV), -100, "mean", 0.0, 16)
+
+
+def test_page_signature_chunked_linear_cross_entropy():
+    from lm_head_cross_pass_amd import chunked_linear_cross_entropy, linear_cross_entropy
+    X, W, t = workloads.small_linear_ce(96, 64, 700, n_ignored=4, seed=23)
+    grads = []
+    for fn in (lambda x, w: chunked_linear_cross_entropy(x, w, t.to(DEV), -100, "mean", 1e-4,
+                                                         "fp32", chunk_size=32),
+               lambda x, w: linear_cross_entropy(x, w, t.to(DEV), -100, "mean", 1e-4, 32, "fp32")):
+        Xd = X.to(DEV).requires_grad_(True)
+        Wd = W.to(DEV).requires_grad_(True)
+        loss = fn(Xd, Wd)
+        loss.backward()
+        grads.append((loss.detach(), Xd.grad, Wd.grad))
+    torch.cuda.synchronize()
+    for a, b in zip(grads[0], grads[1]):
+        assert torch.equal(a, b)
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4)
+    assert float(grads[0][0]) == pytest.approx(ref["loss"], rel=2e-3)
+    # the default chunk size of the page's signature
+    loss = chunked_linear_cross_entropy(X.to(DEV), W.to(DEV), t.to(DEV))
+    assert float(loss) == pytest.approx(oracle.linear_cross_entropy(X, W, t, -100, "mean", 0.0)["loss"],
+                                        rel=2e-3)

@@ -152,3 +152,17 @@ def test_full_size_rows_sampled():
     _rows_close(loss.cpu()[rows], oracle.cross_entropy_per_row(logits[rows], target[rows], -100))
     ref = oracle.cross_entropy_per_row_vjp(logits[rows], target[rows], g[rows].double(), -100)
     _vjp_close(x[rows.to(DEV)], ref, g[rows], torch.bfloat16)
+
+
+def test_selective_log_softmax_any_leading_shape():
+    # the page's entry takes logits [..., V] and index [...]
+    logits, index = workloads.small_ce(24, 1001, torch.bfloat16, sigma=2.0, seed=31)
+    ref = oracle.selective_log_softmax(logits, index)
+    out3 = F.selective_log_softmax(logits.view(2, 3, 4, 1001).to(DEV), index.view(2, 3, 4).to(DEV))
+    out1 = F.selective_log_softmax(logits[5].to(DEV), index[5].to(DEV))
+    torch.cuda.synchronize()
+    assert out3.shape == (2, 3, 4) and out1.shape == ()
+    _rows_close(out3.reshape(-1), ref)
+    _rows_close(out1.reshape(1), ref[5:6])
+    with pytest.raises(ValueError):
+        F.selective_log_softmax(logits.view(2, 12, 1001).to(DEV), index.to(DEV))
