@@ -14,6 +14,7 @@ from lm_head_cross_pass_amd import _lib
 
 F32, BF16 = _lib.LMX_F32, _lib.LMX_BF16
 MEAN, SUM = _lib.LMX_MEAN, _lib.LMX_SUM
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 A = 1 << 40          # a fake, 256-byte aligned device address
 WS = 1 << 20
 
@@ -285,3 +286,36 @@ def test_linear_loss_logits_argument_errors():
     assert f(None, A, 0, 64, 1000, BF16, None, 1000, None) == _lib.LMX_OK
     assert _lib.linear_loss_workspace_bytes(64, 64, 1000, BF16, 16, 0) > 0
     assert _lib.linear_loss_workspace_bytes(64, 64, 1000, F32, 16, 0) == 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/lmx.h compiles as C99 and C++ and a C program links against
+    liblmx.so and calls the host-only entry points (no GPU needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    inc = os.path.join(ROOT, "include")
+    src = tmp_path / "t.c"
+    src.write_text(
+        '#include "lmx.h"\n#include <stdio.h>\n#include <string.h>\n'
+        "int main(void) {\n"
+        "  if (strcmp(lmx_status_string(LMX_OK), \"ok\") != 0) return 1;\n"
+        "  if (lmx_scale(0, 0, -1, LMX_BF16, 0, 0) != LMX_ERR_SIZE) return 2;\n"
+        "  if (ce_workspace_bytes(16, 1000, LMX_F16) == 0) return 3;\n"
+        "  if (linear_ce_chunk_rows(16384, 128256, 2048) != 2048) return 4;\n"
+        "  printf(\"ok\\n\");\n  return 0;\n}\n")
+    exe = tmp_path / "t"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", inc, str(src), "-o", str(exe),
+                        "-L", libdir, "-llmx", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+    gxx = shutil.which("g++")
+    if gxx is not None:
+        r = subprocess.run([gxx, "-std=c++17", "-fsyntax-only", "-Wall", "-Werror", "-x", "c++",
+                            "-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
