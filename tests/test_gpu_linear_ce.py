@@ -305,3 +305,31 @@ def test_page_signature_chunked_linear_cross_entropy():
     loss = chunked_linear_cross_entropy(X.to(DEV), W.to(DEV), t.to(DEV))
     assert float(loss) == pytest.approx(oracle.linear_cross_entropy(X, W, t, -100, "mean", 0.0)["loss"],
                                         rel=2e-3)
+
+
+@pytest.mark.parametrize("BT,D,V,chunk", [(1, 8, 5, 0), (3, 16, 7, 1), (513, 8, 31, 256),
+                                          (40, 24, 2, 16)])
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_tiny_edges(BT, D, V, chunk, dtype):
+    # one row, the smallest D the operand alignment allows, two classes, a
+    # chunk of one row, a ragged last chunk of one row
+    X, W, t = workloads.small_linear_ce(BT, D, V, dtype=dtype, n_ignored=BT // 8, seed=BT * D + V)
+    lt, gt = TOL[dtype]
+    for red, z in (("mean", 1e-4), ("sum", 0.5)):
+        ref = oracle.linear_cross_entropy(X, W, t, -100, red, z)
+        for accum in ("fp32", "weight"):
+            loss, gx, gw, n, bad = _run(X, W, t, red, z, chunk, accum)
+            assert int(n) == ref["n_valid"] and int(bad) == 0
+            assert float(loss) == pytest.approx(ref["loss"], rel=lt)
+            if accum == "weight":
+                emu = oracle.linear_cross_entropy(X, W, t, -100, red, z, "weight",
+                                                  chunk_size=olce_chunk(BT, V, chunk))
+                assert _grad_ok(gw, emu["grad_weight"], dtype)
+            else:
+                assert _grad_ok(gw, ref["grad_weight"], dtype)
+            assert _grad_ok(gx, ref["grad_inputs"], dtype)
+
+
+def olce_chunk(BT, V, chunk):
+    from lm_head_cross_pass_amd import _lib
+    return int(_lib.linear_ce_chunk_rows(BT, V, chunk))
