@@ -419,6 +419,22 @@ def main() -> int:
                                 "sample": f"first {rows} of {ce_w.B} rows of the CE workload "
                                           f"in blocks of {blk} (loss and gradient, fp64), "
                                           f"{dt:.1f} s"}
+    if not args.no_cpu and "linear" in legs:
+        import oracle
+        # the linear-CE oracle on the first rows of the linear workload: logits,
+        # loss, grad_inputs rows and the full grad_weight of those rows, in fp64
+        R = 1536
+        log(f"cpu_baseline: fp64 linear-CE oracle on {R} rows of {lin_w.name}")
+        Xs, Ws, ts = X[:R].cpu(), Wt.cpu(), tl[:R].cpu()
+        t0 = time.perf_counter()
+        oracle.linear_cross_entropy(Xs, Ws, ts, -100, lin_w.reduction, lin_w.z_loss)
+        ldt = time.perf_counter() - t0
+        lfl = 6.0 * R * lin_w.V * lin_w.D
+        line.setdefault("linear_ce", {})["cpu_baseline"] = {
+            "value": round(lfl / ldt / 1e12, 4), "unit": "TFLOP/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"first {R} of {lin_w.BT} rows of the linear-CE workload (loss, grad_inputs "
+                      f"rows, grad_weight, fp64), {ldt:.1f} s"}
     print(json.dumps(line), flush=True)
     return 0
 
