@@ -21,7 +21,7 @@ The per-row term ``logsumexp(logits) - logits[target]`` is also how the nuvec
 loss at ``z = 0`` equals ``gather(log_softmax(x), t)`` as on the greyhound page's
 ``selective_log_softmax`` entry; both serve as pins in the tests.
 
-Readings where the page is silent (each also listed in the design doc):
+Readings where the page is silent:
 
 * ``mean`` with N = 0 gives ``0/0 = nan`` and all-zero gradients;
 * a row is ignored exactly when ``target == ignore_index``, even when

@@ -13,7 +13,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   also receives the forward's loss; it does not change the value, so the
   definition here does not use it.)
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * ``ignore_index`` as in ``cross_entropy``: a row whose target equals it has
   loss 0 and a zero gradient row (the FastOp page has no ignore index; any
