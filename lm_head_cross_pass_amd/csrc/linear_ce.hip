@@ -69,6 +69,13 @@ struct EpiOut {
   int64_t ldp;
   const int64_t* mean_count;   // non-null: scale the products by 1 / *mean_count
 
+  // The same epilogue for the sub-matrix starting at (rows, cols) (direct stores).
+  EpiOut shifted(int64_t rows, int64_t cols) const {
+    EpiOut e = *this;
+    e.out = out + rows * ldo + cols;
+    return e;
+  }
+
   template <int BM, int BN, int FM, int FN>
   __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int split,
                       const GemmShape& g, uint16_t*) {
@@ -112,6 +119,14 @@ struct EpiDw {
   int64_t ld;
   int mode;
   const int64_t* mean_count;   // non-null: scale the products by 1 / *mean_count
+
+  // The same epilogue for the sub-matrix starting at (rows, cols).
+  EpiDw shifted(int64_t rows, int64_t cols) const {
+    EpiDw e = *this;
+    if (acc32 != nullptr) e.acc32 = acc32 + rows * ld + cols;
+    if (out16 != nullptr) e.out16 = out16 + rows * ld + cols;
+    return e;
+  }
 
   template <int MODE, int FM, int FN>
   __device__ void apply(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int n0, const GemmShape& g,
@@ -272,6 +287,51 @@ int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
+// A GEMM on large tiles whose last wave of workgroups would leave most CUs
+// idle: the rows (or columns) that make up that wave go to a second launch on
+// small tiles, whose work items are a quarter the size, so the tail is spread
+// over the chip. Applies to unsplit GEMMs with a direct-store epilogue.
+template <int SCHED, typename E, typename Epi>
+int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t stream) {
+  const int64_t tiles = static_cast<int64_t>(g.tiles_m) * g.tiles_n;
+  const int64_t full = (tiles / 256) * 256;
+  const int64_t rem = tiles - full;
+  if (g.ksplit != 1 || full == 0 || rem == 0 || rem * 3 > 256) {
+    return launch_gemm<SCHED, E>(g, kTileL, epi, stream);
+  }
+  // split along the dimension with more tiles, keeping whole large tiles in
+  // the first launch
+  GemmShape a = g, b = g;
+  if (g.tiles_n >= g.tiles_m) {
+    const int n1 = static_cast<int>(full / g.tiles_m);   // large-tile columns kept
+    const int cols = n1 * kTileL;
+    if (n1 <= 0 || cols >= g.N) return launch_gemm<SCHED, E>(g, kTileL, epi, stream);
+    a.N = cols;
+    a.b_rows = g.b_rows < cols ? g.b_rows : cols;
+    a.tiles_n = n1;
+    b.B = g.B + static_cast<int64_t>(cols) * g.ldb;
+    b.N = g.N - cols;
+    b.b_rows = g.b_rows > cols ? g.b_rows - cols : 0;
+    b.tiles_m = (g.M + kTileS - 1) / kTileS;
+    b.tiles_n = (b.N + kTileS - 1) / kTileS;
+    int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
+    if (st != LMX_OK) return st;
+    return launch_gemm<SCHED, E>(b, kTileS, epi.shifted(0, cols), stream);
+  }
+  const int m1 = static_cast<int>(full / g.tiles_n);       // large-tile rows kept
+  const int rows = m1 * kTileL;
+  if (m1 <= 0 || rows >= g.M) return launch_gemm<SCHED, E>(g, kTileL, epi, stream);
+  a.M = rows;
+  a.tiles_m = m1;
+  b.A = g.A + static_cast<int64_t>(rows) * g.lda;
+  b.M = g.M - rows;
+  b.tiles_m = (b.M + kTileS - 1) / kTileS;
+  b.tiles_n = (g.N + kTileS - 1) / kTileS;
+  int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
+  if (st != LMX_OK) return st;
+  return launch_gemm<SCHED, E>(b, kTileS, epi.shifted(rows, 0), stream);
+}
+
 // The large tile when it yields at least one workgroup per CU of the chip
 // (256 CUs), possibly with up to `max_split` K splits, else the small one.
 int pick_tile(int64_t M, int64_t N, int max_split = 1) {
@@ -312,17 +372,28 @@ int transpose_pad(const uint16_t* src, int64_t ld_src, int R, int Cs, uint16_t* 
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
-// K splits of the grad_inputs product: enough (split, tile) pairs to give every
-// CU its resident workgroups, but at least 4 K steps per split.
-int dx_ksplit(int64_t C, int64_t D, int64_t ldv) {
-  const int tile = pick_tile(C, D, 2);
-  const int64_t tiles = ((C + tile - 1) / tile) * ((D + tile - 1) / tile);
-  const int64_t slots = tile == kTileL ? 256 : 512;
+// Tile and K splits of a chunk's grad_inputs product (C x D outputs, K = ldv):
+// the large tile whenever K splits of at least 8 steps each let its tiles
+// occupy most of the chip's 256 CUs in one wave (a small hidden size gives few
+// tiles but a long K; a work item more than 256 would start a second wave of
+// workgroups, measured 45% slower at D = 768), else the small tile, also split
+// to fill the chip.
+struct DxPlan {
+  int tile;
+  int ksplit;
+};
+DxPlan dx_plan(int64_t C, int64_t D, int64_t ldv) {
   const int64_t ksteps = ldv / kGemmBK;
-  int64_t s = (slots + tiles - 1) / tiles;
-  if (s > ksteps / 4) s = ksteps / 4;
-  if (s < 1) s = 1;
-  return static_cast<int>(s);
+  const int64_t tl = ((C + kTileL - 1) / kTileL) * ((D + kTileL - 1) / kTileL);
+  int64_t sl = 256 / tl;
+  if (sl > ksteps / 8) sl = ksteps / 8;
+  if (sl < 1) sl = 1;
+  if (tl * sl >= 192) return {kTileL, static_cast<int>(sl)};
+  const int64_t ts = ((C + kTileS - 1) / kTileS) * ((D + kTileS - 1) / kTileS);
+  int64_t ss = (512 + ts - 1) / ts;
+  if (ss > ksteps / 4) ss = ksteps / 4;
+  if (ss < 1) ss = 1;
+  return {kTileS, static_cast<int>(ss)};
 }
 
 // grad_inputs rows of one chunk: G [rows, lda_g] times W, with W^T [D, ldv] as
@@ -333,7 +404,7 @@ template <typename E>
 int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_t* wt,
                       int64_t ldv, int rows, int D, int64_t chunk, int ksplit, float* dxp,
                       uint16_t* gx, int64_t ldx, const int64_t* mean_count, hipStream_t stream) {
-  const int tile = pick_tile(chunk, D, 2);   // the tile the workspace was sized for
+  const int tile = dx_plan(chunk, D, ldv).tile;   // the plan the workspace was sized for
   GemmShape gs = make_shape(g, lda_g, wt, ldv, rows, D, D, k_len, ksplit, tile);
   EpiOut<E> e{gx, ldx, dxp, D, mean_count};
   int st = launch_gemm<1, E>(gs, tile, e, stream);
@@ -358,7 +429,8 @@ int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int
   const int tile = pick_tile(V, D);
   GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
   EpiDw<E> e{dw, gw, ldw, mode, mean_count};
-  return launch_gemm<1, E>(gs, tile, e, stream);
+  return tile == kTileL ? launch_gemm_split_tail<1, E>(gs, e, stream)
+                        : launch_gemm<1, E>(gs, tile, e, stream);
 }
 
 }  // namespace
@@ -381,7 +453,7 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   const int64_t C = chunk > 0 ? chunk : 1;
   w.ldv = round_up64(V, kLdvAlign);
   w.ldc = round_up64(C, kLdcAlign);
-  w.ksplit = dx_ksplit(C, D, w.ldv);
+  w.ksplit = dx_plan(C, D, w.ldv).ksplit;
   const int64_t nchunks = BT > 0 ? (BT + C - 1) / C : 0;
   // fp32 accumulation takes the grad_weight product of several chunks at once
   // (K = group ldc): as many chunks as G^T of 1 GiB holds, so the fp32
@@ -458,7 +530,8 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
       const int tile = pick_tile(rows, ldv);
       GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
       EpiOut<E> e{z, ldv, nullptr, 0, nullptr};
-      st = launch_gemm<1, E>(g, tile, e, stream);
+      st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
+                          : launch_gemm<1, E>(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
     // 3. cross-entropy of the chunk rows, G written over Z, loss terms
@@ -511,7 +584,8 @@ int linear_loss_logits_run(const uint16_t* xc, const uint16_t* w, int rows, int 
   const int tile = pick_tile(rows, V);
   GemmShape g = make_shape(xc, D, w, D, rows, V, V, D, 1, tile);
   EpiOut<E> e{logits, ld_logits, nullptr, 0, nullptr};
-  return launch_gemm<1, E>(g, tile, e, stream);
+  return tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
+                        : launch_gemm<1, E>(g, tile, e, stream);
 }
 
 template <typename E>

@@ -133,3 +133,18 @@ def test_grouped_grad_weight_products_generic():
     assert float(loss) == pytest.approx(float(loss_f), rel=1e-5)
     assert _rel(gx, gx_f.double().cpu()) <= 1e-2
     assert _rel(gw, gw_f.double().cpu()) <= 1e-2
+
+
+def test_split_tail_launches_generic():
+    # D = 768 and V = 50256: the chunk's logits product has 4 x 197 large tiles,
+    # so its last columns go to a second launch on small tiles; grad_weight
+    # likewise splits its last rows
+    BT, D, V = 2048, 768, 50256
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=30, seed=41)
+    loss, gx, gw = F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV), F.cross_entropy_loss_and_grad,
+                                             (t.to(DEV),), chunk_size=1024)
+    torch.cuda.synchronize()
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0, block_rows=512)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
