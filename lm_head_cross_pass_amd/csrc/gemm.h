@@ -29,7 +29,8 @@
 // * optional split-K: blockIdx enumerates (k-split, tile) pairs and each
 //   split covers a contiguous range of K steps;
 // * workgroup ids are remapped so that each of the 8 XCDs works on a
-//   contiguous range of tiles (tiles that share A or B panels share an L2).
+//   contiguous range of tiles (tiles that share A or B panels share an L2),
+//   whatever the grid size.
 //
 // The epilogue is a functor called with the accumulators (see linear_ce.hip).
 #pragma once
@@ -138,12 +139,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 }
 
 // Maps blockIdx.x to (split, tile_m, tile_n): tiles of one XCD are contiguous,
-// and within that range the m index runs fastest.
+// and within that range the m index runs fastest. The hardware hands workgroup
+// b to XCD b % 8, so XCD x receives workgroups x, x + 8, ...: nb / 8 of them,
+// one more for the first nb % 8 XCDs; they take the consecutive work items
+// from x (nb / 8) + min(x, nb % 8) on, for any grid size.
 __device__ __forceinline__ void gemm_tile_of_block(const GemmShape& g, int& split, int& tm,
                                                    int& tn) {
   const int nb = gridDim.x;
-  int b = blockIdx.x;
-  if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
+  const int x = static_cast<int>(blockIdx.x) % 8, k = static_cast<int>(blockIdx.x) / 8;
+  const int q = nb / 8, r = nb % 8;
+  const int b = x * q + (x < r ? x : r) + k;
   const int tiles = g.tiles_m * g.tiles_n;
   split = b / tiles;
   const int t = b % tiles;
