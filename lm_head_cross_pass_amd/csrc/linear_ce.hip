@@ -411,6 +411,9 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   if (ksplit > ksteps) ksplit = ksteps > 0 ? ksteps : 1;
   g.ksteps_per_split = (ksteps + ksplit - 1) / ksplit;
   g.ksplit = ksteps > 0 ? (ksteps + g.ksteps_per_split - 1) / g.ksteps_per_split : 1;
+  g.at_out = nullptr;
+  g.ld_at = 0;
+  g.at_cols = 0;
   return g;
 }
 
@@ -450,13 +453,20 @@ DxPlan dx_plan(int64_t C, int64_t D, int64_t ldv) {
 // grad_inputs rows of one chunk: G [rows, lda_g] times W, with W^T [D, ldv] as
 // the K-contiguous operand over K = k_len vocabulary columns, scaled by
 // 1 / *mean_count when that is given; split-K partials in dxp when the layout
-// chose splits.
+// chose splits. With gt_out, the product also writes G^T (gt_out[v * ld_gt +
+// r] for r < gt_cols, zeros for r >= rows) from the G tiles it loads, in place
+// of a separate transpose; the caller passes it only when the chunk's tiles
+// cover all gt_cols columns (a full chunk).
 template <typename E>
 int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_t* wt,
                       int64_t ldv, int rows, int D, int64_t chunk, int ksplit, float* dxp,
-                      uint16_t* gx, int64_t ldx, const int64_t* mean_count, hipStream_t stream) {
+                      uint16_t* gx, int64_t ldx, const int64_t* mean_count, uint16_t* gt_out,
+                      int64_t ld_gt, int gt_cols, hipStream_t stream) {
   const int tile = dx_plan(chunk, D, ldv).tile;   // the plan the workspace was sized for
   GemmShape gs = make_shape(g, lda_g, wt, ldv, rows, D, D, k_len, ksplit, tile);
+  gs.at_out = gt_out;   // optional: G^T written by the product that reads G
+  gs.ld_at = ld_gt;
+  gs.at_cols = gt_cols;
   EpiOut<E> e{gx, ldx, dxp, D, mean_count, staged_ok(gx, ldx, D)};
   int st = launch_gemm<1, E>(gs, tile, e, stream);
   if (st != LMX_OK) return st;
@@ -602,13 +612,18 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
       st = ce_rows_enqueue(cp, p.dtype, stream);
       if (st != LMX_OK) return st;
     }
-    // 4. G^T for the grad_weight product
-    st = transpose_pad(z, ldv, rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
-    if (st != LMX_OK) return st;
+    // 4. G^T for the grad_weight product: written by step 5's product, which
+    // loads every tile of G anyway, except for a ragged last chunk
+    const bool fuse_gt = rows == p.chunk;
+    if (!fuse_gt) {
+      st = transpose_pad(z, ldv, rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
+      if (st != LMX_OK) return st;
+    }
     // 5. grad_inputs rows
     st = chunk_grad_inputs<E>(z, ldv, static_cast<int>(ldv), wt, ldv, rows, D, p.chunk,
                               static_cast<int>(wl.ksplit), dxp, p.grad_x + r0 * p.D, p.D,
-                              mean_count, stream);
+                              mean_count, fuse_gt ? gt + slot * ldc : nullptr, ldk,
+                              static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
     // 6. grad_weight, once per group of chunks
     if (slot == grp - 1 || c == nchunks - 1) {
@@ -659,10 +674,16 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   }
   st = transpose_pad(p.xc, p.D, p.rows, D, xt + slot * ldc, ldk, static_cast<int>(ldc), stream);
   if (st != LMX_OK) return st;
-  st = transpose_pad(p.g, p.ld_g, p.rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc), stream);
-  if (st != LMX_OK) return st;
+  const bool fuse_gt = p.rows == p.chunk;   // G^T from the grad_inputs product
+  if (!fuse_gt) {
+    st = transpose_pad(p.g, p.ld_g, p.rows, V, gt + slot * ldc, ldk, static_cast<int>(ldc),
+                       stream);
+    if (st != LMX_OK) return st;
+  }
   st = chunk_grad_inputs<E>(p.g, p.ld_g, V, wt, ldv, p.rows, D, p.chunk,
-                            static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, nullptr, stream);
+                            static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, nullptr,
+                            fuse_gt ? gt + slot * ldc : nullptr, ldk, static_cast<int>(ldc),
+                            stream);
   if (st != LMX_OK) return st;
   // grad_weight, once per group of chunks (the group's G^T and X^T columns
   // stay in the workspace between the calls)
