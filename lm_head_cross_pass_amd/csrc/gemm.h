@@ -159,8 +159,22 @@ __device__ __forceinline__ void gemm_tile_of_block(const GemmShape& g, int& spli
   const int tiles = g.tiles_m * g.tiles_n;
   split = b / tiles;
   const int t = b % tiles;
-  tm = t % g.tiles_m;
-  tn = t / g.tiles_m;
+  // tiles in groups of kGroupM tile rows, tile row fastest within a group: the
+  // 32 workgroups an XCD runs at once share 8 A bands and 4 B bands instead of
+  // one B band and 32 A bands of a tall grid. The rows past the last whole group
+  // are a group of their own (all of them when tiles_m < kGroupM).
+  constexpr int kGroupM = 8;
+  const int full = g.tiles_m / kGroupM * kGroupM;
+  if (t < full * g.tiles_n) {
+    const int per_group = kGroupM * g.tiles_n;
+    const int w = t % per_group;
+    tm = t / per_group * kGroupM + w % kGroupM;
+    tn = w / kGroupM;
+  } else {
+    const int w = t - full * g.tiles_n, rem = g.tiles_m - full;
+    tm = full + w % rem;
+    tn = w / rem;
+  }
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone): at most N of this
