@@ -82,7 +82,7 @@ struct LinearCeWorkspace {
   int64_t ldv;              // padded vocabulary stride of the chunk buffers
   int64_t ldc;              // padded chunk-row stride of the transposed buffers
   int64_t ksplit;           // K splits of the grad_inputs GEMM
-  int64_t dw_group;         // chunks per grad_weight product (fp32 mode: as many as 1 GiB of G^T holds; else 1)
+  int64_t dw_group;         // chunks per grad_weight product (fp32 mode: as many as 2 GiB of G^T holds; else 1)
   int64_t ldk;              // row stride of G^T and X_c^T: dw_group * ldc
   size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, dxp_off, dw_off, total;
 };

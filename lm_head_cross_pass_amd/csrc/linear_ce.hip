@@ -21,8 +21,8 @@
 // below its smallest subnormal (2^-24) at the batch sizes of the workload.
 // Finally the fixed-order loss reduction. In 'fp32' accumulation dW lives in
 // an fp32 workspace and the last product's epilogue writes the rounded 16-bit
-// result; there step 6 runs once per group of chunks (as many as 1 GiB of G^T
-// holds: two at a vocabulary of 128256 and chunks of 2048), on the group's
+// result; there step 6 runs once per group of chunks (as many as 2 GiB of G^T
+// holds: four at a vocabulary of 128256 and chunks of 2048), on the group's
 // columns of G^T and X^T together (K = group ldc, ldk = group ldc; a last,
 // partial group runs on the chunks it has), which divides the passes over
 // the fp32 accumulator by the group size. In
@@ -45,6 +45,7 @@ constexpr int kTileS = 128;       // small GEMM tile (BM = BN), two workgroups p
 constexpr int kTileL = 256;       // large GEMM tile, one workgroup per CU
 constexpr int kLdvAlign = 256;    // vocabulary padding of the chunk buffers
 constexpr int kLdcAlign = 64;     // chunk-row padding of the transposed buffers
+constexpr int64_t kGtGroupBytes = int64_t{1} << 31;   // G^T budget of one grad_weight group
 constexpr size_t kWsAlign = 256;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -517,13 +518,13 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.ksplit = dx_plan(C, D, w.ldv).ksplit;
   const int64_t nchunks = BT > 0 ? (BT + C - 1) / C : 0;
   // fp32 accumulation takes the grad_weight product of several chunks at once
-  // (K = group ldc): as many chunks as G^T of 1 GiB holds, so the fp32
+  // (K = group ldc): as many chunks as G^T of 2 GiB holds, so the fp32
   // accumulator is read and written once per group instead of once per chunk
   // (in the fused and the generic path alike)
   w.dw_group = 1;
   if (accum == LMX_ACC_F32 && nchunks > 1) {
     const int64_t per_chunk = w.ldv * w.ldc * 2;
-    int64_t gsz = (int64_t{1} << 30) / per_chunk;
+    int64_t gsz = kGtGroupBytes / per_chunk;
     if (gsz > nchunks) gsz = nchunks;
     // the GEMM addresses 256 rows of G^T / X^T with 32-bit byte offsets
     const int64_t gmax = ((int64_t{1} << 31) - 1) / (256 * 2 * w.ldc);
