@@ -525,6 +525,10 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   if (accum == LMX_ACC_F32 && nchunks > 1) {
     const int64_t per_chunk = w.ldv * w.ldc * 2;
     int64_t gsz = kGtGroupBytes / per_chunk;
+    // when G^T of every chunk fits in the group budget plus the fp32
+    // accumulator's bytes, one group takes them all: a single product over
+    // K = BT writes the rounded 16-bit grad_weight and no accumulator is kept
+    if (nchunks * per_chunk <= kGtGroupBytes + V * D * 4) gsz = nchunks;
     if (gsz > nchunks) gsz = nchunks;
     // the GEMM addresses 256 rows of G^T / X^T with 32-bit byte offsets
     const int64_t gmax = ((int64_t{1} << 31) - 1) / (256 * 2 * w.ldc);
@@ -545,7 +549,8 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.xt_off = take(static_cast<size_t>(D) * w.ldk * 2);
   w.wt_off = take(static_cast<size_t>(D) * w.ldv * 2);
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
-  w.dw_off = take(accum == LMX_ACC_F32 && nchunks > 1 ? static_cast<size_t>(V) * D * 4 : 0);
+  w.dw_off = take(accum == LMX_ACC_F32 && nchunks > w.dw_group ? static_cast<size_t>(V) * D * 4
+                                                                 : 0);
   w.total = off;
   return w;
 }

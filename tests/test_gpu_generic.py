@@ -109,13 +109,13 @@ def test_vocabulary_must_give_16_byte_gradient_rows():
 
 
 def test_grouped_grad_weight_products_generic():
-    """Five chunks of 2048 rows at V = 128256 through the generic path: fp32
-    accumulation takes the grad_weight product once per pair of chunks (the
-    pair's G^T columns wait in the workspace between calls), then the last
-    chunk alone; checked against the oracle on sampled rows and against the
-    fused linear_ce on everything."""
+    """Nine chunks of 2048 rows at V = 128256 through the generic path: fp32
+    accumulation takes the grad_weight product once per group of four chunks
+    (the group's G^T columns wait in the workspace between calls): a first
+    group, a middle group, then the last chunk alone; checked against the
+    oracle on sampled rows and against the fused linear_ce on everything."""
     from oracle import linear_ce as olce
-    BT, D, V, C = 5 * 2048, 64, 128256, 2048
+    BT, D, V, C = 9 * 2048, 64, 128256, 2048
     X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=200, seed=13)
     Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
     loss, gx, gw = F.chunked_linear_loss_fwd(Xd, Wd, F.cross_entropy_loss_and_grad, (td,),

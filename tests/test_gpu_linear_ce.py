@@ -178,11 +178,12 @@ def test_workload_bt8192_d768_v50257_full():
 
 
 def test_grouped_grad_weight_products_sampled():
-    """Five chunks of 2048 rows at V = 128256: fp32 accumulation groups two
-    chunks per grad_weight product (G^T of 1 GiB), so the products are a first
-    pair (fp32 store), a middle pair (read-modify-write) and the last chunk alone
-    (read-modify-write and bf16 cast); checked on sampled rows."""
-    BT, D, V, C = 5 * 2048, 64, 128256, 2048
+    """Nine chunks of 2048 rows at V = 128256: fp32 accumulation groups four
+    chunks per grad_weight product (G^T of 2 GiB; all nine do not fit that plus
+    the accumulator), so the products are a first group (fp32 store), a middle
+    group (read-modify-write) and the last chunk alone (read-modify-write and
+    bf16 cast); checked on sampled rows."""
+    BT, D, V, C = 9 * 2048, 64, 128256, 2048
     X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=200, seed=12)
     loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, C, "fp32")
     g = torch.Generator().manual_seed(3)
