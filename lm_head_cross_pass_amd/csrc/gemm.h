@@ -82,12 +82,18 @@ struct GemmShape {
   int ksplit;            // number of K splits (1 = none)
   int ksteps_per_split;  // K steps per split
   // Optional (at_out != nullptr): every A tile also written out transposed,
-  // at_out[k * ld_at + m] = A[m][k], by one of the tiles_n workgroups that
-  // load it (the one whose tile_n is the K step modulo tiles_n); columns
-  // m >= at_cols are left alone. at_out must hold round_up(K, 64) rows.
+  // at_out[k * ld_at + m] = A[m][k] for k < K, by one of the tiles_n
+  // workgroups that load it (the one whose tile_n is the K step modulo
+  // tiles_n); columns m >= at_cols are left alone. Rows of A past M read as
+  // zero, so columns M .. at_cols - 1 receive zeros.
   uint16_t* at_out;
   int64_t ld_at;
   int at_cols;
+  // The same for B (bt_out[k * ld_bt + n] = B[n][k], columns n < bt_cols), by
+  // the one of the tiles_m workgroups whose tile_m is the K step modulo tiles_m.
+  uint16_t* bt_out;
+  int64_t ld_bt;
+  int bt_cols;
 };
 
 // Block tile BM x BN: 2 x 2 waves for 128 x 128, 2 x 4 waves for 256 x 256;
@@ -249,24 +255,26 @@ __device__ __forceinline__ void gemm_load_frags(const char* smem, const int* a_o
     bfr[j] = *reinterpret_cast<const u32x4*>(smem + (b_off[j] ^ flip));
 }
 
-// Writes the A tile of one K step (BM rows x kGemmBK in the LDS stage at
-// `sa`, 16-byte pieces of a row XOR-swizzled) transposed to
-// at_out[(kbase + kk) * ld_at + m0 + r]. A thread takes an 8 x 8 block (8 rows,
-// one 16-byte piece of each), transposes it in registers with byte permutes
-// and stores 8 pieces of 8 rows each.
-template <typename C, int BM>
-__device__ __forceinline__ void gemm_store_a_transposed(const char* sa, const GemmShape& g,
-                                                        int m0, int kbase) {
-  constexpr int RB = BM / 8;                  // 8-row blocks
+// Writes the operand tile of one K step (R rows x kGemmBK in the LDS stage at
+// `st`, 16-byte pieces of a row XOR-swizzled) transposed to
+// out[(kbase + kk) * ld + r0 + r] for kbase + kk < K and r0 + r < cols. A
+// thread takes an 8 x 8 block (8 rows, one 16-byte piece of each), transposes
+// it in registers with byte permutes and stores 8 pieces of 8 rows each.
+template <typename C, int R>
+__device__ __forceinline__ void gemm_store_tile_transposed(const char* st, uint16_t* out,
+                                                           int64_t ld, int r0, int cols,
+                                                           int kbase, int K) {
+  constexpr int RB = R / 8;                   // 8-row blocks
   constexpr int BLOCKS = RB * (kGemmBK / 8);
   for (int t = static_cast<int>(threadIdx.x); t < BLOCKS; t += C::THREADS) {
     const int b = t % RB, c = t / RB;         // rows 8b .. 8b + 7, k piece c
-    if (m0 + 8 * b + 8 > g.at_cols) continue; // at_cols is a multiple of 8
+    // cols and K are multiples of 8: a block is wholly inside or outside
+    if (r0 + 8 * b + 8 > cols || kbase + 8 * c >= K) continue;
     u32x4 in[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * b + i;
-      in[i] = *reinterpret_cast<const u32x4*>(sa + r * C::ROWB + ((c ^ lds_swz<C::CPR>(r)) << 4));
+      in[i] = *reinterpret_cast<const u32x4*>(st + r * C::ROWB + ((c ^ lds_swz<C::CPR>(r)) << 4));
     }
     // out piece j (k = 8c + j) holds element j of every row: word q of it is
     // (row 2q, row 2q + 1) at k; element j of a row is half (j & 1) of word j / 2
@@ -282,8 +290,8 @@ __device__ __forceinline__ void gemm_store_a_transposed(const char* sa, const Ge
         o[q] = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
                        : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
       }
-      *reinterpret_cast<u32x4*>(g.at_out + static_cast<int64_t>(kbase + 8 * c + j) * g.ld_at +
-                                m0 + 8 * b) = o;
+      *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(kbase + 8 * c + j) * ld + r0 + 8 * b) =
+          o;
     }
   }
 }
@@ -429,7 +437,13 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     }
     gemm_mfma_slice<C, E>(acc, fa1, fb1);
     if (g.at_out != nullptr && ks % g.tiles_n == tn) {
-      gemm_store_a_transposed<C, BM>(smem + cur_bytes, g, m0, ks * kGemmBK);
+      gemm_store_tile_transposed<C, BM>(smem + cur_bytes, g.at_out, g.ld_at, m0, g.at_cols,
+                                        ks * kGemmBK, g.K);
+    }
+    if (g.bt_out != nullptr && ks % g.tiles_m == tm) {
+      static_assert(C::A_STAGE == C::B_STAGE, "B stages addressed with the A stage offset");
+      gemm_store_tile_transposed<C, BN>(smem + C::B_BASE + cur_bytes, g.bt_out, g.ld_bt, n0,
+                                        g.bt_cols, ks * kGemmBK, g.K);
     }
     if (ks + 1 < ke) {
       // step ks + 1 landed: the copies issued after it (up to AHEAD - 1 steps)

@@ -4,14 +4,17 @@
 // page, "chunked_linear_loss" and "chunked_linear_cross_entropy").
 //
 // Per call:   count valid targets (global N, needed before any gradient is
-//             scaled); W^T [D, ldv] (zero-padded) for the grad_inputs GEMM.
+//             scaled).
 // Per chunk of C rows (r0 .. r0 + C'):
 //   1. X_c^T into its columns of X^T [D, ldk]          transpose
-//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM
+//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM; chunk 0's
+//      also writes W^T [D, ldv] (zero-padded) for step 5 from the W tiles
 //   3. the cross-entropy row kernel on Z, in place: loss terms and the
 //      gradient of the summed loss, G = (1 + 2 z lse) softmax - onehot
 //                                                      same kernel as ce_fwd_bwd
-//   4. G^T into its columns of G^T [ldv, ldk]          transpose
+//   4. G^T into its columns of G^T [ldv, ldk]          written by step 5's GEMM
+//                                                      (a transpose for a ragged
+//                                                      last chunk)
 //   5. grad_inputs[r0:] = s G W                        MFMA GEMM (split-K if the
 //                                                      tile count cannot fill the chip)
 //   6. dW (+)= s G^T X_c                               MFMA GEMM, accumulate epilogue
@@ -366,6 +369,12 @@ int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t strea
     b.b_rows = g.b_rows > cols ? g.b_rows - cols : 0;
     b.tiles_m = (g.M + kTileS - 1) / kTileS;
     b.tiles_n = (b.N + kTileS - 1) / kTileS;
+    // transposed copies: A's whole tile rows are in both launches (the first
+    // writes them); B's columns continue in the second
+    b.at_out = nullptr;
+    a.bt_cols = g.bt_cols < cols ? g.bt_cols : cols;
+    if (g.bt_out != nullptr) b.bt_out = g.bt_out + cols;
+    b.bt_cols = g.bt_cols > cols ? g.bt_cols - cols : 0;
     int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
     if (st != LMX_OK) return st;
     return launch_gemm<SCHED, E>(b, kTileS, epi.shifted(0, cols), stream);
@@ -379,6 +388,10 @@ int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t strea
   b.M = g.M - rows;
   b.tiles_m = (b.M + kTileS - 1) / kTileS;
   b.tiles_n = (g.N + kTileS - 1) / kTileS;
+  a.at_cols = g.at_cols < rows ? g.at_cols : rows;
+  if (g.at_out != nullptr) b.at_out = g.at_out + rows;
+  b.at_cols = g.at_cols > rows ? g.at_cols - rows : 0;
+  b.bt_out = nullptr;
   int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
   if (st != LMX_OK) return st;
   return launch_gemm<SCHED, E>(b, kTileS, epi.shifted(rows, 0), stream);
@@ -415,6 +428,9 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.at_out = nullptr;
   g.ld_at = 0;
   g.at_cols = 0;
+  g.bt_out = nullptr;
+  g.ld_bt = 0;
+  g.bt_cols = 0;
   return g;
 }
 
@@ -580,8 +596,8 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
     return finish_enqueue(row_loss, 0, n_ws, p.reduction, p.loss, stream);
   }
-  st = transpose_pad(p.w, p.D, V, D, wt, ldv, static_cast<int>(ldv), stream);
-  if (st != LMX_OK) return st;
+  // W^T [D, ldv] for the grad_inputs products is written by chunk 0's logits
+  // product, which loads every tile of W (zero rows past V give the padding)
   const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t r0 = c * p.chunk;
@@ -596,6 +612,11 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     {
       const int tile = pick_tile(rows, ldv);
       GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
+      if (c == 0) {
+        g.bt_out = wt;
+        g.ld_bt = ldv;
+        g.bt_cols = static_cast<int>(ldv);
+      }
       EpiOut<E> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
       st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
                           : launch_gemm<1, E>(g, tile, e, stream);
