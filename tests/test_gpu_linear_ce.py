@@ -68,8 +68,8 @@ CASES = [
     (257, 128, 4099, 100),
     (300, 256, 8192, 0),       # default chunk size
     (1024, 64, 257, 1024),     # one chunk of 1024 rows; ksplit > 1 path
-    (256, 64, 1000, 64),       # four chunks: two paired grad_weight products
-    (250, 80, 777, 50),        # five chunks: two pairs and a last chunk alone
+    (256, 64, 1000, 64),       # four chunks, one grad_weight product over all of them
+    (250, 80, 777, 50),        # five chunks, the last one ragged
 ]
 
 
@@ -172,6 +172,21 @@ def test_workload_bt8192_d768_v50257_full():
     loss, gx, gw, n, bad = _run(X, W, t, w.reduction, w.z_loss, w.chunk_size, "fp32")
     assert int(n) == w.BT - w.n_ignored == 7782
     ref = oracle.linear_cross_entropy(X, W, t, -100, w.reduction, w.z_loss, block_rows=1024)
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+def test_split_tail_along_rows():
+    # one chunk of 8448 rows at V = 2048: its logits product has 33 x 8 large
+    # tiles, so the last 256 rows go to a second launch on small tiles (the
+    # split along the dimension with more tiles); the first launch alone
+    # writes W^T for grad_inputs
+    BT, D, V = 8448, 64, 2048
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=40, seed=43)
+    loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, BT, "fp32")
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, block_rows=1024)
+    assert int(n) == BT - 40 and int(bad) == 0
     assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
     assert _rel(gx, ref["grad_inputs"]) <= 1e-2
     assert _rel(gw, ref["grad_weight"]) <= 1e-2
