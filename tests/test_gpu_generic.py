@@ -135,6 +135,28 @@ def test_grouped_grad_weight_products_generic():
     assert _rel(gw, gw_f.double().cpu()) <= 1e-2
 
 
+@pytest.mark.parametrize("accum", ("fp32", "weight"))
+def test_workspace_contents_do_not_matter_generic(accum):
+    # three chunks, the last ragged: a workspace full of NaN bit patterns gives
+    # the same bits as a zeroed one (every padding entry read is written first)
+    from lm_head_cross_pass_amd import _lib
+    BT, D, V, C = 250, 72, 776, 100
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=6, seed=29)
+    Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
+    nbytes = _lib.linear_loss_workspace_bytes(BT, D, V, _lib.LMX_BF16, C,
+                                              0 if accum == "fp32" else 1)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(F.chunked_linear_loss_fwd(Xd, Wd, F.cross_entropy_loss_and_grad, (td,),
+                                              chunk_size=C, grad_weight_accum_dtype=accum,
+                                              workspace=ws))
+    torch.cuda.synchronize()
+    a, b = outs
+    assert float(a[0]) == float(b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert not bool(torch.isnan(a[2].float()).any())
+
+
 def test_split_tail_launches_generic():
     # D = 768 and V = 50256: the chunk's logits product has 4 x 197 large tiles,
     # so its last columns go to a second launch on small tiles; grad_weight

@@ -166,6 +166,30 @@ def test_repeatable_bitwise():
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
 
 
+@pytest.mark.parametrize("BT,D,V,chunk,accum", [
+    (256, 128, 3000, 64, "fp32"),     # full chunks: G^T from the grad_inputs GEMM
+    (250, 72, 777, 64, "fp32"),       # ragged last chunk, padded vocabulary and K
+    (250, 72, 777, 64, "weight"),
+    (8448, 64, 2048, 8448, "fp32"),   # split-tail launches along rows
+])
+def test_workspace_contents_do_not_matter(BT, D, V, chunk, accum):
+    # every padding row and column the GEMMs read is written by the same call:
+    # a workspace full of NaN bit patterns gives the same bits as a zeroed one
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=7, seed=17)
+    Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
+    from lm_head_cross_pass_amd import _lib
+    nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, _lib.LMX_BF16, chunk,
+                                            0 if accum == "fp32" else 1)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(F.linear_ce(Xd, Wd, td, -100, "mean", 1e-4, chunk, accum, workspace=ws))
+    torch.cuda.synchronize()
+    a, b = outs
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert not bool(torch.isnan(a[2].float()).any())
+
+
 def test_workload_bt8192_d768_v50257_full():
     w = workloads.LCE_BT8192_D768_V50257
     X, W, t = workloads.linear_ce_inputs(w)
