@@ -22,7 +22,10 @@ in GB/s of its own algorithmic bytes; ``linear_ce.generic_chunked_loss`` times t
 generic chunked linear loss with the library's cross-entropy as the caller's loss
 on the linear-CE inputs; ``fp16`` times the CE and the fused linear-CE on the
 same values converted to IEEE binary16. ``cpu_baseline`` is the fp64 oracle timed
-on the host on a bounded sample of the same CE workload.
+on the host on a bounded sample of the same CE workload. ``traffic`` (HBM bytes)
+and the linear leg's ``mfma_busy`` (each GEMM's matrix-core busy share and the
+clock under that load) come from the committed rocprofv3 counter summaries in
+``profiles/`` and are null when those were taken on other kernel code.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows,generic,fp16] [--no-cpu]
 """
@@ -63,9 +66,9 @@ def source_digest(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(counter_file: str, digest: str, key: str = "hbm_bytes_per_launch"):
-    """HBM bytes per launch (or per call) from a committed counter summary, if it
-    matches the current source."""
+def stored_values(counter_file: str, digest: str):
+    """The `key = value` lines of a committed counter summary, if it matches the
+    current source (else None)."""
     path = os.path.join(PROFILES, counter_file)
     if not os.path.exists(path):
         return None
@@ -74,7 +77,14 @@ def stored_traffic(counter_file: str, digest: str, key: str = "hbm_bytes_per_lau
         if "=" in ln and not ln.lstrip().startswith("#"):
             k, v = ln.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != digest or key not in vals:
+    return vals if vals.get("source_digest") == digest else None
+
+
+def stored_traffic(counter_file: str, digest: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per call) from a committed counter summary, if it
+    matches the current source."""
+    vals = stored_values(counter_file, digest)
+    if vals is None or key not in vals:
         return None
     return float(vals[key])
 
@@ -213,14 +223,24 @@ def main() -> int:
     if "linear" in legs:
         flops = 6.0 * lin_w.BT * lin_w.V * lin_w.D
         tf = flops / (lin_ms * 1e-3) / 1e12
+        lin_digest = source_digest("gemm.h", "linear_ce.hip", "ce.hip", "common.h")
         lin_traffic = stored_traffic("linear_ce_bt16384_d4096_v128256_c2048.counters.txt",
-                                     source_digest("gemm.h", "linear_ce.hip", "ce.hip", "common.h"),
-                                     "hbm_bytes_per_call")
+                                     lin_digest, "hbm_bytes_per_call")
+        # matrix-core busy share of each GEMM's cycles and the clock under that
+        # load, from the committed counter summary of the same code
+        mv = stored_values("linear_ce_bt16384_d4096_v128256_c2048.mfma.txt", lin_digest)
+        mfma_busy = None
+        if mv is not None:
+            mfma_busy = {k[len("mfma_busy_"):]: float(v) for k, v in mv.items()
+                         if k.startswith("mfma_busy_")}
+            if "clock_ghz_under_load" in mv:
+                mfma_busy["clock_ghz"] = float(mv["clock_ghz_under_load"])
         lin = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(lin_ms, 3),
                "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": lin_traffic,
                             "algorithmic_flops_per_call": flops,
+                            "mfma_busy": mfma_busy,
                             "kernel": "whole linear_ce call (gemm_nt_kernel x3 per chunk + CE)"}}
         # 'weight' accumulation, timed on its own
         if args.weight_steps > 0:
