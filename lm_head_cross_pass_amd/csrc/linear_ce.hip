@@ -22,13 +22,14 @@
 // accumulators in the epilogues rather than to G: G is held in the 16-bit
 // input format, and for fp16 the mean's scaled probabilities p/N would fall
 // below its smallest subnormal (2^-24) at the batch sizes of the workload.
-// Finally the fixed-order loss reduction. In 'fp32' accumulation dW lives in
-// an fp32 workspace and the last product's epilogue writes the rounded 16-bit
-// result; there step 6 runs once per group of chunks (as many as 2 GiB of G^T
-// holds: four at a vocabulary of 128256 and chunks of 2048), on the group's
-// columns of G^T and X^T together (K = group ldc, ldk = group ldc; a last,
-// partial group runs on the chunks it has), which divides the passes over
-// the fp32 accumulator by the group size. In
+// Finally the fixed-order loss reduction. In 'fp32' accumulation step 6 runs
+// once per group of chunks, on the group's columns of G^T and X^T together
+// (K = group ldc, ldk = group ldc; a last, partial group runs on the chunks it
+// has): as many chunks as 2 GiB of G^T holds (four at a vocabulary of 128256
+// and chunks of 2048), with dW in an fp32 workspace that the last product's
+// epilogue rounds to 16 bits, or all chunks in one product that writes the
+// 16-bit result directly when their G^T fits that budget plus the fp32
+// accumulator's bytes (16384 rows of 4096 at that vocabulary). In
 // 'weight' accumulation the 16-bit grad_weight itself is updated per chunk
 // (rounded to nearest even after each chunk, as the accumulation mode
 // prescribes; ldk = ldc).
