@@ -28,6 +28,9 @@ clock under that load) come from the committed rocprofv3 counter summaries in
 ``profiles/`` and are null when those were taken on other kernel code.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows,generic,fp16] [--no-cpu]
+
+``--legs small`` (not in the default) times the two smaller workloads, CE
+[4096, 50257] and linear-CE 8192 x 768 x 50257, under ``small_workloads``.
 """
 from __future__ import annotations
 
@@ -97,7 +100,8 @@ def main() -> int:
     ap.add_argument("--legs", default="ce,linear,rows,generic,fp16",
                     help="ce, linear, rows (per-row entry points; needs ce), generic (the "
                          "generic chunked linear loss; needs linear), fp16 (the ce and linear "
-                         "legs' workloads in fp16)")
+                         "legs' workloads in fp16), small (the two smaller workloads, not in "
+                         "the default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--weight-steps", type=int, default=3)
     args = ap.parse_args()
@@ -419,6 +423,68 @@ def main() -> int:
             log(f"fp16 linear-CE: {ms:.3f} ms, {tf:.0f} TFLOP/s")
             del X16, W16, gx16, gw16
         line["fp16"] = f16
+
+    # ------------------------------------------------------------ smaller workloads
+    # the two smaller workloads (parity cases of the tests, not bench lines),
+    # timed only when asked for: CE [4096, 50257] bf16, mean, z 1e-4, out of
+    # place, and linear-CE [8192, 768] x [50257, 768], chunk 1024, fp32 accumulation
+    if "small" in legs:
+        sm = {}
+        cw = workloads.CE_B4096_V50257_BF16
+        xh, th = workloads.ce_inputs(cw)
+        x2, t2 = xh.to(dev), th.to(dev)
+        g2 = torch.empty_like(x2)
+        ws2 = torch.empty(_lib.ce_workspace_bytes(cw.B, cw.V, _lib.LMX_BF16), dtype=torch.uint8,
+                          device=dev)
+        o2 = [torch.empty((), dtype=torch.float32, device=dev),
+              torch.empty((), dtype=torch.int64, device=dev),
+              torch.empty((), dtype=torch.int32, device=dev)]
+
+        def ce2():
+            _lib.check("ce_fwd_bwd", _lib.ce_fwd_bwd(
+                x2.data_ptr(), g2.data_ptr(), t2.data_ptr(), cw.B, cw.V, _lib.LMX_BF16, -100,
+                _lib.LMX_MEAN, cw.z_loss[0], o2[0].data_ptr(), o2[1].data_ptr(), o2[2].data_ptr(),
+                ws2.data_ptr(), ws2.numel(), stream.cuda_stream))
+        lw = workloads.LCE_BT8192_D768_V50257
+        Xh, Wh, tlh = workloads.linear_ce_inputs(lw)
+        X4, W4, t4 = Xh.to(dev), Wh.to(dev), tlh.to(dev)
+        gx4, gw4 = torch.empty_like(X4), torch.empty_like(W4)
+        ws4 = torch.empty(_lib.linear_ce_workspace_bytes(lw.BT, lw.D, lw.V, _lib.LMX_BF16,
+                                                         lw.chunk_size, _lib.LMX_ACC_F32),
+                          dtype=torch.uint8, device=dev)
+
+        def lin4():
+            _lib.check("linear_ce", _lib.linear_ce(
+                X4.data_ptr(), W4.data_ptr(), t4.data_ptr(), lw.BT, lw.D, lw.V, _lib.LMX_BF16,
+                -100, _lib.LMX_MEAN, lw.z_loss, lw.chunk_size, _lib.LMX_ACC_F32,
+                o2[0].data_ptr(), gx4.data_ptr(), gw4.data_ptr(), o2[1].data_ptr(),
+                o2[2].data_ptr(), ws4.data_ptr(), ws4.numel(), stream.cuda_stream))
+
+        def timed(fn, n):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+        ms = timed(ce2, 20)
+        nbytes = 2 * cw.B * cw.V * 2 + 8 * cw.B
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        sm[cw.name] = {"value": round(gbps, 1), "unit": "GB/s", "ms_per_call": round(ms, 4),
+                       "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        log(f"{cw.name}: {ms * 1e3:.1f} us, {gbps:.0f} GB/s")
+        ms = timed(lin4, 20)
+        flops = 6.0 * lw.BT * lw.V * lw.D
+        tf = flops / (ms * 1e-3) / 1e12
+        sm[lw.name] = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(ms, 4),
+                       "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"{lw.name}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        line["small_workloads"] = sm
+        del x2, g2, X4, W4, gx4, gw4
 
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu and "ce" in legs:
