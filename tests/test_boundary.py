@@ -319,3 +319,20 @@ def test_header_is_plain_c_and_links(tmp_path):
         r = subprocess.run([gxx, "-std=c++17", "-fsyntax-only", "-Wall", "-Werror", "-x", "c++",
                             "-I", inc, str(src)], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # with no built library the binding raises (there is no CPU fallback), and
+    # the torch-facing functions refuse host tensors instead of computing on them
+    import torch
+    from lm_head_cross_pass_amd import functional as F
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "liblmx.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _lib.load()
+    with pytest.raises(ValueError, match="no CPU path"):
+        F.cross_entropy(torch.zeros(2, 8), torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="no CPU path"):
+        F.linear_cross_entropy(torch.zeros(2, 8, dtype=torch.bfloat16),
+                               torch.zeros(4, 8, dtype=torch.bfloat16),
+                               torch.zeros(2, dtype=torch.int64))
