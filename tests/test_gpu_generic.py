@@ -157,12 +157,13 @@ def test_workspace_contents_do_not_matter_generic(accum):
     assert not bool(torch.isnan(a[2].float()).any())
 
 
-def test_split_tail_launches_generic():
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_split_tail_launches_generic(dtype):
     # D = 768 and V = 50256: the chunk's logits product has 4 x 197 large tiles,
     # so its last columns go to a second launch on small tiles; grad_weight
     # likewise splits its last rows
     BT, D, V = 2048, 768, 50256
-    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=30, seed=41)
+    X, W, t = workloads.small_linear_ce(BT, D, V, dtype=dtype, n_ignored=30, seed=41)
     loss, gx, gw = F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV), F.cross_entropy_loss_and_grad,
                                              (t.to(DEV),), chunk_size=1024)
     torch.cuda.synchronize()

@@ -201,6 +201,21 @@ def test_workload_bt8192_d768_v50257_full():
     assert _rel(gw, ref["grad_weight"]) <= 1e-2
 
 
+def test_weight_accumulation_with_split_tail_launches():
+    # D = 768, V = 50257, two chunks of 1024 in 'weight' mode: each chunk's
+    # grad_weight product stores (then read-modify-writes) the bf16 gradient
+    # through a large-tile launch and a small-tile launch for its last rows
+    BT, D, V, C = 2048, 768, 50257, 1024
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=20, seed=47)
+    emu = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, "weight", chunk_size=C,
+                                      block_rows=512)
+    loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, C, "weight")
+    assert int(n) == BT - 20 and int(bad) == 0
+    assert float(loss) == pytest.approx(emu["loss"], rel=2e-3)
+    assert _rel(gx, emu["grad_inputs"]) <= 1e-2
+    assert _rel(gw, emu["grad_weight"]) <= 1e-2
+
+
 def test_split_tail_along_rows():
     # one chunk of 8448 rows at V = 2048: its logits product has 33 x 8 large
     # tiles, so the last 256 rows go to a second launch on small tiles (the
