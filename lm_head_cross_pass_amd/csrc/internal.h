@@ -84,7 +84,8 @@ struct LinearCeWorkspace {
   int64_t ksplit;           // K splits of the grad_inputs GEMM
   int64_t dw_group;         // chunks per grad_weight product (fp32 mode: as many as 2 GiB of G^T holds; else 1)
   int64_t ldk;              // row stride of G^T and X_c^T: dw_group * ldc
-  size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, dxp_off, dw_off, total;
+  size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, dxp_off, dw_off, dwp_off, total;
+  size_t dwp_bytes;         // K-split partials of grad_weight's last rows (0: none)
 };
 // generic = true: the layout of the generic chunked loss (no chunk logits
 // buffer: the caller holds them; one grad_weight product per chunk).

@@ -317,6 +317,31 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<uint2*>(out + static_cast<int64_t>(row) * ldo + col) = o;
 }
 
+// grad_weight rows [rows0, V) from the K-split partials of their large-tile
+// launch (already scaled by 1 / N when the mean asks for it): the sum over the
+// splits in a fixed order, then the store or accumulation of `mode`, as the
+// grad_weight epilogue does it for the other rows. acc32 / out16 point at the
+// first of these rows.
+template <typename E>
+__global__ __launch_bounds__(256) void dw_tail_reduce_kernel(const float* __restrict__ partial,
+                                                             int ksplit, int M, int N,
+                                                             float* acc32, uint16_t* out16,
+                                                             int64_t ld, int mode) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(M) * N) return;
+  const int row = static_cast<int>(i / N), col = static_cast<int>(i % N);
+  float v = 0.f;
+  for (int s = 0; s < ksplit; ++s) v += partial[(static_cast<int64_t>(s) * M + row) * N + col];
+  const int64_t e = static_cast<int64_t>(row) * ld + col;
+  switch (mode) {
+    case kDwStoreF32: acc32[e] = v; break;
+    case kDwAddF32: acc32[e] = acc32[e] + v; break;
+    case kDwAddF32ToW16: out16[e] = E::narrow(acc32[e] + v); break;
+    case kDwStoreW16: out16[e] = E::narrow(v); break;
+    default: out16[e] = E::narrow(E::widen(out16[e]) + v); break;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* p, int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
@@ -498,16 +523,71 @@ int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_
   return LMX_OK;
 }
 
+// The grad_weight product's last rows on large tiles with K split, in place of
+// the small-tile second launch: when its large tiles leave a last wave under a
+// third full and the split goes along the rows (launch_gemm_split_tail's
+// case), rows0 .. V - 1 take ksplit large-tile workgroups per tile (one wave
+// in all, at least 8 K steps each), and a reduction sums the splits.
+struct DwTail {
+  int rows0;
+  int ksplit;   // 1: no K-split tail
+};
+
+DwTail dw_tail_plan(int64_t V, int64_t D, int64_t K) {
+  DwTail t{0, 1};
+  const int64_t tm = (V + kTileL - 1) / kTileL, tn = (D + kTileL - 1) / kTileL;
+  const int64_t tiles = tm * tn, full = tiles / 256 * 256, rem = tiles - full;
+  if (full == 0 || rem == 0 || rem * 3 > 256 || tn >= tm) return t;
+  const int64_t m1 = full / tn;
+  if (m1 <= 0 || m1 * kTileL >= V) return t;
+  int64_t ks = 256 / ((tm - m1) * tn);
+  const int64_t ksteps = (K + kGemmBK - 1) / kGemmBK;
+  if (ks > ksteps / 8) ks = ksteps / 8;
+  if (ks < 2) return t;
+  t.rows0 = static_cast<int>(m1 * kTileL);
+  t.ksplit = static_cast<int>(ks);
+  return t;
+}
+
+size_t dw_tail_bytes(int64_t V, int64_t D, int64_t K) {
+  const DwTail t = dw_tail_plan(V, D, K);
+  return t.ksplit > 1 ? static_cast<size_t>(t.ksplit) * (V - t.rows0) * D * 4 : 0;
+}
+
 // grad_weight product G^T X over K columns of G^T [V, ldk] and X^T [D, ldk],
 // scaled by 1 / *mean_count when that is given, stored or accumulated
-// according to `mode`.
+// according to `mode`. tailp (tail_bytes of workspace) holds the K-split
+// partials of the last rows when dw_tail_plan splits them.
 template <typename E>
 int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int K, int V, int D,
                         float* dw, uint16_t* gw, int64_t ldw, int mode,
-                        const int64_t* mean_count, hipStream_t stream) {
+                        const int64_t* mean_count, float* tailp, size_t tail_bytes,
+                        hipStream_t stream) {
   const int tile = pick_tile(V, D);
   GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
   EpiDw<E> e{dw, gw, ldw, mode, mean_count};
+  if (tile == kTileL && tailp != nullptr && dw_tail_bytes(V, D, K) <= tail_bytes) {
+    const DwTail tp = dw_tail_plan(V, D, K);
+    if (tp.ksplit > 1) {
+      GemmShape a = gs;
+      a.M = tp.rows0;
+      a.tiles_m = tp.rows0 / kTileL;
+      int st = launch_gemm<1, E>(a, kTileL, e, stream);
+      if (st != LMX_OK) return st;
+      const int rows = V - tp.rows0;
+      GemmShape b = make_shape(gt + static_cast<int64_t>(tp.rows0) * ldk, ldk, xt, ldk, rows, D,
+                               D, K, tp.ksplit, kTileL);
+      EpiOut<E> eo{nullptr, 0, tailp, D, mean_count, 0};   // fp32 partials per split
+      st = launch_gemm<1, E>(b, kTileL, eo, stream);
+      if (st != LMX_OK) return st;
+      const EpiDw<E> et = e.shifted(tp.rows0, 0);
+      const int64_t total = static_cast<int64_t>(rows) * D;
+      hipLaunchKernelGGL(dw_tail_reduce_kernel<E>, dim3(static_cast<unsigned>((total + 255) / 256)),
+                         dim3(256), 0, stream, tailp, b.ksplit, rows, D, et.acc32, et.out16, ldw,
+                         mode);
+      return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
+    }
+  }
   return tile == kTileL ? launch_gemm_split_tail<1, E>(gs, e, stream)
                         : launch_gemm<1, E>(gs, tile, e, stream);
 }
@@ -568,6 +648,9 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
   w.dw_off = take(accum == LMX_ACC_F32 && nchunks > w.dw_group ? static_cast<size_t>(V) * D * 4
                                                                  : 0);
+  // K-split partials of grad_weight's last rows (the largest K any product has)
+  w.dwp_bytes = dw_tail_bytes(V, D, w.ldk);
+  w.dwp_off = take(w.dwp_bytes);
   w.total = off;
   return w;
 }
@@ -584,6 +667,7 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
   uint16_t* wt = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
+  float* dwp = reinterpret_cast<float*>(ws + wl.dwp_off);
   const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
   const int64_t ldv = wl.ldv, ldc = wl.ldc, ldk = wl.ldk, grp = wl.dw_group;
   const int64_t* mean_count = p.reduction == LMX_MEAN ? n_ws : nullptr;
@@ -664,7 +748,7 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
         mode = first ? kDwStoreW16 : kDwAddW16;
       }
       st = grad_weight_product<E>(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw,
-                                  p.grad_w, p.D, mode, mean_count, stream);
+                                  p.grad_w, p.D, mode, mean_count, dwp, wl.dwp_bytes, stream);
       if (st != LMX_OK) return st;
     }
   }
@@ -691,6 +775,7 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   uint16_t* wt = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
+  float* dwp = reinterpret_cast<float*>(ws + wl.dwp_off);
   const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
   const int64_t ldv = wl.ldv, ldc = wl.ldc, ldk = wl.ldk, grp = wl.dw_group;
   const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
@@ -725,7 +810,7 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
     mode = first ? kDwStoreW16 : kDwAddW16;
   }
   return grad_weight_product<E>(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw,
-                                p.grad_w, p.D, mode, nullptr, stream);
+                                p.grad_w, p.D, mode, nullptr, dwp, wl.dwp_bytes, stream);
 }
 
 int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream) {

@@ -216,6 +216,27 @@ def test_weight_accumulation_with_split_tail_launches():
     assert _rel(gw, emu["grad_weight"]) <= 1e-2
 
 
+def test_grouped_products_with_k_split_tail_sampled():
+    """V = 86016 at D = 64 gives grad_weight 336 large tiles: the last 80 row
+    tiles run with K split in three, and their partials are reduced into the
+    fp32 accumulator (store, then add) or, in the last group, added and rounded
+    to bf16. Thirteen chunks of 2048 make groups of 6, 6 and 1; checked on
+    sampled rows, the split rows among them."""
+    BT, D, V, C = 13 * 2048, 64, 86016, 2048
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=100, seed=53)
+    loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, C, "fp32")
+    g = torch.Generator().manual_seed(4)
+    rows = torch.randperm(BT, generator=g)[:16].tolist()
+    vrows = (torch.randperm(V, generator=g)[:12].tolist() + [65535, 65536, 70000, V - 1]
+             + [int(t[rows[0]])])
+    ref = olce.linear_cross_entropy_sampled(X, W, t, rows, vrows, -100, "mean", 1e-4,
+                                            block_rows=1024)
+    assert int(n) == BT - 100 and int(bad) == 0
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx.cpu()[rows], ref["grad_inputs_rows"]) <= 1e-2
+    assert _rel(gw.cpu()[vrows], ref["grad_weight_rows"]) <= 1e-2
+
+
 def test_split_tail_along_rows():
     # one chunk of 8448 rows at V = 2048: its logits product has 33 x 8 large
     # tiles, so the last 256 rows go to a second launch on small tiles (the
