@@ -161,14 +161,16 @@ LMX_API size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype);
  *                 the matmuls take 16-bit operands).
  *   chunk_size    rows per chunk; 0 picks a size from a 1 GiB budget for the
  *                 chunk's logits; < 0 is LMX_ERR_CHUNK.
- *   accum         LMX_ACC_F32: grad_weight is accumulated in an fp32
- *                 workspace and rounded once; LMX_ACC_WEIGHT: it is
+ *   accum         LMX_ACC_F32: grad_weight is accumulated in fp32 (within a
+ *                 product over a group of chunks, and across groups in an fp32
+ *                 workspace) and rounded once; LMX_ACC_WEIGHT: it is
  *                 accumulated in grad_weight itself, rounding after each chunk.
  *   loss          one fp32 on the device.
  *   grad_inputs   [BT, D] 16-bit output, 16-byte aligned.
  *   grad_weight   [V, D]  16-bit output, 16-byte aligned.
  *   n_valid, bad_target as for ce_fwd_bwd (may be NULL).
- *   workspace     >= linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum).
+ *   workspace     >= linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum);
+ *                 its contents on entry do not matter.
  * Outputs must not overlap the inputs (LMX_ERR_ALIAS).
  */
 LMX_API int linear_ce(const void* inputs, const void* weight, const int64_t* target,
