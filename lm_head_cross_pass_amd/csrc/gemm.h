@@ -167,7 +167,7 @@ __device__ __forceinline__ void gemm_tile_of_block(const GemmShape& g, int& spli
   const int t = b % tiles;
   // tiles in groups of kGroupM tile rows, tile row fastest within a group: the
   // 32 workgroups an XCD runs at once share 4 A bands and 8 B bands instead of
-  // one B band and 32 A bands of a tall grid (4 measured faster than 2, 8 and
+  // one B band and 32 A bands of a tall grid (4 measured faster than 2, 3, 6, 8 and
   // 16 on the 126976-row grad_weight product). The rows past the last whole
   // group are a group of their own (all of them when tiles_m < kGroupM).
   constexpr int kGroupM = 4;
