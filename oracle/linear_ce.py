@@ -40,6 +40,62 @@ def _finish_loss(row_loss_sum_terms, n_valid: int, reduction: str) -> float:
     return total
 
 
+def linear_cross_entropy_chunks(inputs: torch.Tensor, weight: torch.Tensor,
+                                target: torch.Tensor, ignore_index: int = -100,
+                                reduction: str = "mean", z_loss_multiplier: float = 0.0,
+                                chunk_rows: int = 256):
+    """The linear cross-entropy chunk by chunk, in fp64, in the order of the rows.
+
+    Yields one dict per chunk of ``chunk_rows`` rows (the last one may be shorter):
+    ``r0``, ``r1`` (the rows), ``lse`` and ``row_loss`` of those rows, their
+    ``grad_inputs`` rows ``G_c @ weight`` and the chunk's product
+    ``partial = G_c.T @ inputs[r0:r1]`` (its share of grad_weight); ``n_valid``
+    and ``scale`` are those of the whole batch (one global N for the mean).
+    """
+    BT, D = inputs.shape
+    V = weight.shape[0]
+    n_valid, valid = count_valid(target, ignore_index, V)
+    scale = reduction_scale(n_valid, reduction)
+    W = weight.to(torch.float64)
+    for r0 in range(0, BT, chunk_rows):
+        r1 = min(BT, r0 + chunk_rows)
+        Xc = inputs[r0:r1].to(torch.float64)
+        logits = Xc @ W.T                                        # [rows, V]
+        lse, rl, G = cross_entropy_rows(logits, target[r0:r1], valid[r0:r1],
+                                        scale, z_loss_multiplier)
+        del logits
+        yield {"r0": r0, "r1": r1, "lse": lse, "row_loss": rl, "grad_inputs": G @ W,
+               "partial": G.T @ Xc, "n_valid": n_valid, "scale": scale}
+
+
+def _rowwise(fn, M: torch.Tensor, workers: int) -> torch.Tensor:
+    """fn applied to row blocks of M (fn is element-wise: the blocking does not
+    change any value), on up to ``workers`` threads."""
+    if workers <= 1 or M.shape[0] < 2 * workers:
+        return fn(M)
+    import concurrent.futures as cf
+    out = torch.empty_like(M)
+    bounds = [(i * M.shape[0] // workers, (i + 1) * M.shape[0] // workers) for i in range(workers)]
+
+    def run(b):
+        out[b[0]:b[1]] = fn(M[b[0]:b[1]])
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(run, bounds))
+    return out
+
+
+def accumulate_weight_dtype(dW: torch.Tensor, partial: torch.Tensor, weight_dtype: torch.dtype,
+                            workers: int = 1) -> torch.Tensor:
+    """One chunk of the ``'weight'`` accumulation: ``rnd(dW + partial)``.
+
+    The running weight gradient is held in the parameter's dtype, so after each
+    chunk the exact sum of the previous value and the chunk's exact product is
+    rounded to nearest even in that dtype (bf16, or fp16 for an fp16 weight).
+    """
+    rnd = round_to_fp16 if weight_dtype == torch.float16 else round_to_bf16
+    return _rowwise(rnd, dW + partial, workers)
+
+
 def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
                          ignore_index: int = -100, reduction: str = "mean",
                          z_loss_multiplier: float = 0.0,
@@ -56,15 +112,6 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
     """
     BT, D = inputs.shape
     V = weight.shape[0]
-    n_valid, valid = count_valid(target, ignore_index, V)
-    scale = reduction_scale(n_valid, reduction)
-    X = inputs.to(torch.float64)
-    W = weight.to(torch.float64)
-    dX = torch.zeros((BT, D), dtype=torch.float64)
-    dW = torch.zeros((V, D), dtype=torch.float64)
-    lse = torch.empty(BT, dtype=torch.float64)
-    row_loss = torch.empty(BT, dtype=torch.float64)
-
     if grad_weight_accum_dtype == "fp32":
         step = block_rows
     elif grad_weight_accum_dtype == "weight":
@@ -73,20 +120,21 @@ def linear_cross_entropy(inputs: torch.Tensor, weight: torch.Tensor, target: tor
         step = chunk_size
     else:
         raise ValueError(f"unknown grad_weight_accum_dtype {grad_weight_accum_dtype!r}")
-    rnd = round_to_fp16 if weight.dtype == torch.float16 else round_to_bf16
-
-    for r0 in range(0, BT, step):
-        r1 = min(BT, r0 + step)
-        logits = X[r0:r1] @ W.T                                  # [rows, V]
-        l, rl, G = cross_entropy_rows(logits, target[r0:r1], valid[r0:r1],
-                                      scale, z_loss_multiplier)
-        lse[r0:r1] = l
-        row_loss[r0:r1] = rl
-        dX[r0:r1] = G @ W                                        # [rows, D]
+    dX = torch.zeros((BT, D), dtype=torch.float64)
+    dW = torch.zeros((V, D), dtype=torch.float64)
+    lse = torch.empty(BT, dtype=torch.float64)
+    row_loss = torch.empty(BT, dtype=torch.float64)
+    n_valid = count_valid(target, ignore_index, V)[0]
+    for ch in linear_cross_entropy_chunks(inputs, weight, target, ignore_index, reduction,
+                                          z_loss_multiplier, step):
+        r0, r1 = ch["r0"], ch["r1"]
+        lse[r0:r1] = ch["lse"]
+        row_loss[r0:r1] = ch["row_loss"]
+        dX[r0:r1] = ch["grad_inputs"]
         if grad_weight_accum_dtype == "fp32":
-            dW.addmm_(G.T, X[r0:r1])                             # exact sum over chunks
+            dW += ch["partial"]                                  # exact sum over chunks
         else:
-            dW = rnd(dW + G.T @ X[r0:r1])                        # rounds between chunks
+            dW = accumulate_weight_dtype(dW, ch["partial"], weight.dtype)   # rounds between chunks
     loss = _finish_loss(row_loss.tolist(), n_valid, reduction)
     return {"loss": loss, "grad_inputs": dX, "grad_weight": dW, "n_valid": n_valid,
             "lse": lse, "row_loss": row_loss}

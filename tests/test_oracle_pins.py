@@ -392,6 +392,63 @@ def test_weight_mode_emulation_follows_the_weight_dtype():
     assert float((many["grad_weight"] - exact["grad_weight"]).abs().max()) <= float(bound)
 
 
+# Hand-worked three-chunk cases of the weight-dtype accumulation (greyhound
+# functional API page, chunked_linear_cross_entropy, grad_weight_accum_dtype:
+# the running gradient is kept in the weight's dtype and rounds between
+# chunks). With a zero weight and V = 2 every logit is 0, so every softmax is
+# exactly (1/2, 1/2); with all targets 1 and the sum reduction each row's
+# logits gradient is (+1/2, -1/2), and the product of chunk c for weight row 0
+# is P_c = (x_2c + x_2c+1) / 2 (D = 1, chunks of two rows). Row 1 is the
+# negation of row 0 (rounding to nearest even is symmetric).
+#
+# bf16 (8 significant bits; spacing 2^-8 in [0.5, 1), 2^-7 in [1, 2), 2^-6 in
+# [2, 4)). In units of 2^-10: x = 1024, 1032, 1040, 1048, 1032, 4, so
+# P = 1028, 1044, 518 and the exact sum is 2590 (2.529296875).
+#   per chunk:      rnd(1028) = 1024 (tie between 1024 and 1032; 1024 even),
+#                   rnd(1024 + 1044 = 2068) = 2064 (2064 or 2080; 4 away),
+#                   rnd(2064 + 518 = 2582) = 2576 (2576 or 2592; 6 away)
+#                   -> 2576 / 1024 = 161/64;
+#   exact, rounded once:          rnd(2590) = 2592 (2 away) -> 81/32;
+#   P_c rounded too:              rnd(1044) = 1040 (tie, even), rnd(518) = 520
+#                                 (tie, even): 1024 + 1040 = 2064,
+#                                 rnd(2064 + 520 = 2584) = 2592 (tie, even);
+#   first rounding skipped:       rnd(1028 + 1044 = 2072) = 2080 (tie, even),
+#                                 rnd(2080 + 518 = 2598) = 2592;
+#   last two chunks together:     rnd(1044 + 518 = 1562) = 1560,
+#                                 rnd(1024 + 1560 = 2584) = 2592 (tie, even).
+# fp16 (11 significant bits) is the same case three bits finer: in units of
+# 2^-13, x = 8192, 8200, 8208, 8216, 8200, 4, P = 8196, 8212, 4102, and the
+# per-chunk result is 20496 / 8192 = 1281/512 where every slip above gives
+# 641/256 (the exact sum is 20510 / 8192).
+_HAND_WORKED = {
+    torch.bfloat16: ([1.0, 1 + 2.0 ** -7, 1 + 2.0 ** -6, 1 + 3 * 2.0 ** -7, 1 + 2.0 ** -7, 2.0 ** -8],
+                     161 / 64, 81 / 32, 2590 / 1024),
+    torch.float16: ([1.0, 1 + 2.0 ** -10, 1 + 2.0 ** -9, 1 + 3 * 2.0 ** -10, 1 + 2.0 ** -10,
+                     2.0 ** -11], 1281 / 512, 641 / 256, 20510 / 8192),
+}
+
+
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_weight_mode_emulation_hand_worked(dtype):
+    xs, per_chunk, slip, exact_sum = _HAND_WORKED[dtype]
+    X = torch.tensor(xs, dtype=torch.float64).to(dtype).reshape(6, 1)
+    assert X.double().flatten().tolist() == xs                  # exact in the format
+    W = torch.zeros(2, 1, dtype=dtype)
+    t = torch.ones(6, dtype=torch.int64)
+    emu = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0, "weight", chunk_size=2)
+    assert emu["grad_weight"].flatten().tolist() == [per_chunk, -per_chunk]
+    assert per_chunk != slip
+    exact = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0)
+    assert exact["grad_weight"].flatten().tolist() == [exact_sum, -exact_sum]
+    rnd = round_to_bf16 if dtype == torch.bfloat16 else round_to_fp16
+    assert float(rnd(torch.tensor([exact_sum]))[0]) == slip
+    # grad_inputs rows: G_r W = 0 for a zero weight
+    assert bool((emu["grad_inputs"] == 0).all())
+    # one chunk of all six rows is the exact sum rounded once
+    one = oracle.linear_cross_entropy(X, W, t, -100, "sum", 0.0, "weight", chunk_size=6)
+    assert one["grad_weight"].flatten().tolist() == [slip, -slip]
+
+
 # ---------------------------------------------------------------- golden fixture
 def test_golden_small_workload_is_reproduced():
     import os
@@ -459,3 +516,38 @@ def test_planted_linear_mistakes_are_caught(monkeypatch):
     assert _fd_linear_error(0.0, "mean", BT=4, D=4, V=4) > 1.0
     monkeypatch.setattr(olce, "linear_cross_entropy", dropped_z)
     assert _fd_linear_error(0.5, "sum") > 1.0
+
+
+@pytest.mark.parametrize("skip", ({1}, {1, 2}, {2}))
+def test_planted_weight_mode_mistakes_are_caught(skip, monkeypatch):
+    # the emulation rounds once per chunk; skipping the rounding after chunk 1
+    # (first rounding missed), after chunks 1 and 2 (exact sum rounded once) or
+    # after chunk 2 alone must fail the hand-worked pin
+    real = olce.round_to_bf16
+    calls = []
+
+    def mutant(v):
+        calls.append(1)
+        return v.clone() if len(calls) in skip else real(v)
+
+    monkeypatch.setattr(olce, "round_to_bf16", mutant)
+    xs, per_chunk, _, _ = _HAND_WORKED[torch.bfloat16]
+    X = torch.tensor(xs, dtype=torch.float64).to(torch.bfloat16).reshape(6, 1)
+    W = torch.zeros(2, 1, dtype=torch.bfloat16)
+    t = torch.ones(6, dtype=torch.int64)
+    emu = olce.linear_cross_entropy(X, W, t, -100, "sum", 0.0, "weight", chunk_size=2)
+    assert len(calls) == 3
+    assert emu["grad_weight"].flatten().tolist() != [per_chunk, -per_chunk]
+
+
+def test_weight_dtype_accumulation_is_blocking_independent():
+    # the element-wise rounding applied to row blocks on several threads gives
+    # the same values as one call over the whole matrix
+    g = torch.Generator().manual_seed(21)
+    dW = round_to_bf16(torch.randn(103, 17, generator=g) * 1e-3)
+    P = torch.randn(103, 17, generator=g) * 1e-3
+    one = olce.accumulate_weight_dtype(dW, P, torch.bfloat16, 1)
+    assert torch.equal(one, round_to_bf16(dW + P))
+    assert torch.equal(olce.accumulate_weight_dtype(dW, P, torch.bfloat16, 4), one)
+    assert torch.equal(olce.accumulate_weight_dtype(dW, P, torch.float16, 3),
+                       round_to_fp16(dW + P))
