@@ -196,7 +196,8 @@ LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int d
  *   inputs_c    [rows, D] 16-bit, 16-byte aligned, D % 8 == 0.
  *   weight      [V, D] 16-bit, 16-byte aligned.
  *   logits      [rows, ld_logits] 16-bit output (ld_logits >= V; columns >= V
- *               are not written), not overlapping the inputs.
+ *               are not written), not overlapping the inputs; ld_logits is
+ *               bounded like V (<= 4194048, LMX_ERR_SIZE beyond).
  * Limits as for linear_ce (LMX_ERR_SIZE); LMX_F32 is LMX_ERR_UNSUPPORTED. No
  * workspace.
  */
@@ -229,7 +230,8 @@ LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t
  *                 LMX_F16 for every 16-bit buffer); rows must be the chunk's
  *                 size (c, or what is left of BT for the last one).
  *   grad_logits   [rows, ld_grad] 16-bit, 16-byte aligned; ld_grad >= V and
- *                 V % 8 == 0 and ld_grad % 8 == 0 (LMX_ERR_ALIGN otherwise).
+ *                 V % 8 == 0 and ld_grad % 8 == 0 (LMX_ERR_ALIGN otherwise);
+ *                 ld_grad <= 4194048 like V (LMX_ERR_SIZE beyond).
  *                 Used as given: any reduction scale is the caller's.
  *   grad_inputs_c [rows, D] 16-bit output for this chunk's rows.
  *   grad_weight   [V, D] 16-bit output / accumulator.

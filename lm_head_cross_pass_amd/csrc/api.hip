@@ -223,8 +223,10 @@ int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, i
                        int64_t V, int dtype, void* logits, int64_t ld_logits, void* stream) {
   if (weight == nullptr || (rows > 0 && (inputs_c == nullptr || logits == nullptr)))
     return LMX_ERR_NULL;
+  // the output's row stride is bounded like V: the GEMM epilogue addresses 256
+  // rows of it with 32-bit byte offsets
   if (rows < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || rows > kLinMaxChunk ||
-      ld_logits < V)
+      ld_logits < V || ld_logits > kLinMaxV)
     return LMX_ERR_SIZE;
   if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
   if (dtype == LMX_F32) return LMX_ERR_UNSUPPORTED;
@@ -249,7 +251,10 @@ int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad
   if (weight == nullptr || grad_weight == nullptr || workspace == nullptr) return LMX_ERR_NULL;
   if (rows > 0 && (inputs_c == nullptr || grad_logits == nullptr || grad_inputs_c == nullptr))
     return LMX_ERR_NULL;
-  if (BT <= 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || ld_grad < V)
+  // the gradient's row stride is bounded like V (256-row operand panels are
+  // addressed with 32-bit byte offsets)
+  if (BT <= 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || ld_grad < V ||
+      ld_grad > kLinMaxV)
     return LMX_ERR_SIZE;
   if (chunk_size < 0) return LMX_ERR_CHUNK;
   if (!dtype_ok(dtype)) return LMX_ERR_ENUM;

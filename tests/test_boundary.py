@@ -260,6 +260,7 @@ def _grads(**kw):
     (dict(g=None), _lib.LMX_ERR_NULL),
     (dict(BT=0), _lib.LMX_ERR_SIZE),
     (dict(ldg=999), _lib.LMX_ERR_SIZE),
+    (dict(ldg=4194048 + 8), _lib.LMX_ERR_SIZE),           # stride beyond the 32-bit panel offsets
     (dict(rows=15), _lib.LMX_ERR_SIZE),                   # not the chunk's size
     (dict(idx=4), _lib.LMX_ERR_CHUNK),                    # 64 / 16 = 4 chunks
     (dict(idx=-1), _lib.LMX_ERR_CHUNK),
@@ -280,6 +281,9 @@ def test_linear_loss_logits_argument_errors():
     f = _lib.linear_loss_logits
     assert f(A, None, 16, 64, 1000, BF16, A + (3 << 34), 1000, None) == _lib.LMX_ERR_NULL
     assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + (3 << 34), 999, None) == _lib.LMX_ERR_SIZE
+    # an output stride beyond what 32-bit offsets over 256 rows reach
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + (3 << 34), 4194048 + 8,
+             None) == _lib.LMX_ERR_SIZE
     assert f(A, A + (1 << 34), 16, 64, 1000, 7, A + (3 << 34), 1000, None) == _lib.LMX_ERR_ENUM
     assert f(A, A + (1 << 34), 16, 60, 1000, BF16, A + (3 << 34), 1000, None) == _lib.LMX_ERR_ALIGN
     assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + 64, 1000, None) == _lib.LMX_ERR_ALIAS
