@@ -97,7 +97,8 @@ enum {
   LMX_ERR_ALIGN = -6,       /* a pointer or leading dimension breaks the alignment rule */
   LMX_ERR_CHUNK = -7,       /* chunk_size < 0 */
   LMX_ERR_UNSUPPORTED = -8, /* a valid combination this library does not implement */
-  LMX_ERR_HIP = -9          /* a HIP runtime call failed while enqueuing */
+  LMX_ERR_HIP = -9,         /* a HIP runtime call failed while enqueuing */
+  LMX_ERR_SCRATCH = -10     /* more rows than ce_fwd_bwd_noalloc's fixed scratch holds */
 };
 
 /*
@@ -136,6 +137,26 @@ LMX_API int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* tar
 
 /* Workspace bytes ce_fwd_bwd needs for these sizes (0 for invalid sizes). */
 LMX_API size_t ce_workspace_bytes(int64_t B, int64_t V, int dtype);
+
+/*
+ * ce_fwd_bwd_noalloc -- ce_fwd_bwd without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and errors as ce_fwd_bwd, minus workspace /
+ * workspace_bytes. The workspace is a fixed array inside the library, one per
+ * GPU, held until the process ends (256 bytes + 4 MiB): it takes at most
+ * 1048576 rows; a larger B returns LMX_ERR_SCRATCH before anything is
+ * enqueued. The call allocates nothing. The first call on a device looks up
+ * the array's device address there (a HIP runtime query, not an allocation).
+ * Every call on one GPU uses that GPU's array, so calls that overlap in time
+ * on one GPU (other streams, other threads) race: serialize them.
+ */
+LMX_API int ce_fwd_bwd_noalloc(const void* logits, void* grad_logits, const int64_t* target,
+                               int64_t B, int64_t V, int dtype, int64_t ignore_index,
+                               int reduction, float z_loss_multiplier,
+                               float* loss, int64_t* n_valid, int32_t* bad_target,
+                               void* stream);
 
 /*
  * linear_ce -- chunked linear cross-entropy, loss plus grad_inputs and grad_weight.

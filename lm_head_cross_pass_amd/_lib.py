@@ -24,6 +24,7 @@ STATUS = {
     0: "LMX_OK", -1: "LMX_ERR_NULL", -2: "LMX_ERR_SIZE", -3: "LMX_ERR_ENUM",
     -4: "LMX_ERR_WORKSPACE", -5: "LMX_ERR_ALIAS", -6: "LMX_ERR_ALIGN",
     -7: "LMX_ERR_CHUNK", -8: "LMX_ERR_UNSUPPORTED", -9: "LMX_ERR_HIP",
+    -10: "LMX_ERR_SCRATCH",
 }
 for _code, _name in STATUS.items():
     globals()[_name] = _code
@@ -35,6 +36,8 @@ _SIGNATURES = {
     "ce_fwd_bwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i64, _i32, _f32,
                           _vp, _vp, _vp, _vp, _sz, _vp]),
     "ce_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "ce_fwd_bwd_noalloc": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i64, _i32, _f32,
+                                  _vp, _vp, _vp, _vp]),
     "linear_ce": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _f32,
                          _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "linear_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32]),
@@ -100,6 +103,13 @@ def ce_fwd_bwd(logits, grad_logits, target, B, V, dtype, ignore_index, reduction
     return load().ce_fwd_bwd(logits, grad_logits, target, B, V, dtype, ignore_index,
                              reduction, z_loss_multiplier, loss, n_valid, bad_target,
                              workspace, workspace_bytes, stream)
+
+
+def ce_fwd_bwd_noalloc(logits, grad_logits, target, B, V, dtype, ignore_index, reduction,
+                       z_loss_multiplier, loss, n_valid, bad_target, stream) -> int:
+    return load().ce_fwd_bwd_noalloc(logits, grad_logits, target, B, V, dtype, ignore_index,
+                                     reduction, z_loss_multiplier, loss, n_valid, bad_target,
+                                     stream)
 
 
 def ce_workspace_bytes(B, V, dtype) -> int:

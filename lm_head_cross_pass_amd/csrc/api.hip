@@ -40,6 +40,27 @@ bool mul_fits(int64_t a, int64_t b, int64_t c) {
 
 namespace lmx {
 
+int ce_args_status(const void* logits, const void* grad_logits, const int64_t* target,
+                   int64_t B, int64_t V, int dtype, int reduction, const float* loss) {
+  if (loss == nullptr) return LMX_ERR_NULL;
+  if (B > 0 && (logits == nullptr || target == nullptr)) return LMX_ERR_NULL;
+  if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
+  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
+  if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
+  const int eb = dtype == LMX_F32 ? 4 : 2;
+  if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
+  const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
+  const uintptr_t pl = reinterpret_cast<uintptr_t>(logits);
+  const uintptr_t pg = reinterpret_cast<uintptr_t>(grad_logits);
+  if (pl % eb != 0 || reinterpret_cast<uintptr_t>(target) % 8 != 0) return LMX_ERR_ALIGN;
+  if (grad_logits != nullptr && (pg % 16) != (pl % 16)) return LMX_ERR_ALIGN;
+  if (grad_logits != nullptr && grad_logits != logits &&
+      overlaps(logits, bytes, grad_logits, bytes))
+    return LMX_ERR_ALIAS;
+  if (grad_logits != nullptr && overlaps(grad_logits, bytes, target, B * 8)) return LMX_ERR_ALIAS;
+  return LMX_OK;
+}
+
 CeWorkspace ce_workspace_layout(int64_t B) {
   CeWorkspace w;
   w.n_valid_off = 0;
@@ -64,6 +85,8 @@ const char* lmx_status_string(int status) {
     case LMX_ERR_CHUNK: return "chunk_size is negative";
     case LMX_ERR_UNSUPPORTED: return "combination not implemented";
     case LMX_ERR_HIP: return "a HIP runtime call failed";
+    case LMX_ERR_SCRATCH:
+      return "more rows than the fixed scratch buffer of the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -77,23 +100,10 @@ int ce_fwd_bwd(const void* logits, void* grad_logits, const int64_t* target, int
                int64_t V, int dtype, int64_t ignore_index, int reduction,
                float z_loss_multiplier, float* loss, int64_t* n_valid, int32_t* bad_target,
                void* workspace, size_t workspace_bytes, void* stream) {
-  if (loss == nullptr || workspace == nullptr) return LMX_ERR_NULL;
-  if (B > 0 && (logits == nullptr || target == nullptr)) return LMX_ERR_NULL;
-  if (B < 0 || !row_fits(V, dtype)) return LMX_ERR_SIZE;
-  if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
-  if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
-  const int eb = dtype == LMX_F32 ? 4 : 2;
-  if (!mul_fits(B, V, eb)) return LMX_ERR_SIZE;
-  const size_t bytes = static_cast<size_t>(B) * static_cast<size_t>(V) * eb;
-  const uintptr_t pl = reinterpret_cast<uintptr_t>(logits);
-  const uintptr_t pg = reinterpret_cast<uintptr_t>(grad_logits);
-  if (pl % eb != 0 || reinterpret_cast<uintptr_t>(target) % 8 != 0) return LMX_ERR_ALIGN;
-  if (grad_logits != nullptr && (pg % 16) != (pl % 16)) return LMX_ERR_ALIGN;
+  if (workspace == nullptr) return LMX_ERR_NULL;
+  const int st = lmx::ce_args_status(logits, grad_logits, target, B, V, dtype, reduction, loss);
+  if (st != LMX_OK) return st;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return LMX_ERR_WORKSPACE;
-  if (grad_logits != nullptr && grad_logits != logits &&
-      overlaps(logits, bytes, grad_logits, bytes))
-    return LMX_ERR_ALIAS;
-  if (grad_logits != nullptr && overlaps(grad_logits, bytes, target, B * 8)) return LMX_ERR_ALIAS;
   const lmx::CeWorkspace wl = lmx::ce_workspace_layout(B);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);

@@ -53,6 +53,11 @@ struct VjpParams {
 };
 int ce_vjp_enqueue(const VjpParams& p, int dtype, hipStream_t stream);
 
+// Host checks of ce_fwd_bwd's arguments other than the workspace (LMX_OK when
+// the call may proceed); no HIP call.
+int ce_args_status(const void* logits, const void* grad_logits, const int64_t* target,
+                   int64_t B, int64_t V, int dtype, int reduction, const float* loss);
+
 // Workspace layout of ce_fwd_bwd.
 struct CeWorkspace {
   size_t n_valid_off, row_loss_off, total;

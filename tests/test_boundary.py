@@ -29,7 +29,7 @@ def built_library():
 
 def test_every_declared_function_is_exported():
     names = _lib.header_functions()
-    assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "linear_ce",
+    assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "ce_fwd_bwd_noalloc", "linear_ce",
                           "linear_ce_workspace_bytes", "linear_ce_chunk_rows",
                           "lmx_status_string", "lmx_copy", "lmx_scale",
                           "selective_log_softmax",
@@ -275,6 +275,23 @@ def _grads(**kw):
 ])
 def test_linear_loss_grads_argument_errors(kw, status):
     assert _grads(**kw) == status
+
+
+def test_noalloc_argument_errors():
+    # host checks return before any HIP call: more rows than the fixed scratch
+    # holds, and the argument errors of ce_fwd_bwd
+    f = _lib.ce_fwd_bwd_noalloc
+    loss, n, bad = A + (3 << 34), A + (3 << 34) + 64, A + (3 << 34) + 128
+    big = (1 << 20) + 1
+    assert f(A, A, A + (2 << 34), big, 1000, BF16, -100, 0, 0.0, loss, n, bad,
+             None) == _lib.LMX_ERR_SCRATCH
+    assert f(A, A, A + (2 << 34), 16, 1000, BF16, -100, 0, 0.0, None, n, bad,
+             None) == _lib.LMX_ERR_NULL
+    assert f(A, A, A + (2 << 34), 16, 1000, 9, -100, 0, 0.0, loss, n, bad,
+             None) == _lib.LMX_ERR_ENUM
+    assert f(A, A + 64, A + (2 << 34), 16, 1000, BF16, -100, 0, 0.0, loss, n, bad,
+             None) == _lib.LMX_ERR_ALIAS
+    assert _lib.status_string(_lib.LMX_ERR_SCRATCH).startswith("more rows")
 
 
 def test_linear_loss_logits_argument_errors():
