@@ -11,13 +11,16 @@ back, then their linear-CE calls, each part after its own warmup;
   fresh logits);
 * chunked linear-CE with inputs [16384, 4096] bf16 ~ N(0, 1), weight
   [128256, 4096] bf16 ~ N(0, 0.02), 2% ignored, chunk 2048, mean, z = 0,
-  fp32 grad_weight accumulation.
+  fp32 grad_weight accumulation, the library's default grad_weight grouping
+  (2 GiB of transposed logits gradient per product: four chunks).
 
 The JSON line reports the CE leg as ``value`` (GB/s of algorithmic traffic:
 one read of the logits, one write of the gradient, the int64 targets) with its
 roofline against the 8 TB/s HBM peak, and the linear-CE leg under
 ``linear_ce`` (TFLOP/s of the three matmuls, 6 BT V D, against the 2.5 PFLOP/s
-dense bf16 MFMA peak), plus its 'weight'-accumulation variant timed on its own.
+dense bf16 MFMA peak) with its workspace bytes, plus, each timed on its own,
+'weight' accumulation and both modes with one grad_weight product over every
+chunk (``one_group``: the G^T budget that holds all eight chunks).
 ``next_rows`` times the per-row entry points on the CE leg's logits (forward-only
 reduced CE, selective_log_softmax, the unreduced per-row CE and its VJP), each
 in GB/s of its own algorithmic bytes; ``linear_ce.generic_chunked_loss`` times the
@@ -29,10 +32,13 @@ and the linear leg's ``mfma_busy`` (each GEMM's matrix-core busy share and the
 clock under that load) come from the committed rocprofv3 counter summaries in
 ``profiles/`` and are null when those were taken on other kernel code.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--legs ce,linear,rows,generic,fp16] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+                    [--legs ce,linear,rows,generic,fp16,small] [--no-cpu]
 
-``--legs small`` (not in the default) times the two smaller workloads, CE
-[4096, 50257] and linear-CE 8192 x 768 x 50257, under ``small_workloads``.
+``small_workloads`` times the two GPT-2-shaped workloads, CE [4096, 50257] and
+linear-CE 8192 x 768 x 50257, each with its roofline fraction and, where a
+counter summary of the same code is committed, its HBM traffic. Every timed
+figure is the mean over back-to-back calls (``ms_median`` beside it).
 """
 from __future__ import annotations
 
@@ -94,16 +100,45 @@ def stored_traffic(counter_file: str, digest: str, key: str = "hbm_bytes_per_lau
     return float(vals[key])
 
 
+def per_call_ms(fn, n: int, warm: int, stream):
+    """Times n calls of fn back to back on `stream` with HIP events between
+    them (after `warm` untimed calls); returns the per-call times in ms."""
+    import torch
+    for _ in range(warm):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def mean_median(ts):
+    import statistics
+    return sum(ts) / len(ts), statistics.median(ts)
+
+
+def gt_group_bytes_all(BT: int, V: int, chunk: int) -> int:
+    """A grad_weight group budget that covers every chunk of the call: the
+    transposed logits gradient of all chunks (vocabulary padded to 256, chunk
+    rows to 64, 2 bytes)."""
+    ldv = (V + 255) // 256 * 256
+    ldc = (chunk + 63) // 64 * 64
+    return (BT + chunk - 1) // chunk * ldv * ldc * 2
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="ce,linear,rows,generic,fp16",
+    ap.add_argument("--legs", default="ce,linear,rows,generic,fp16,small",
                     help="ce, linear, rows (per-row entry points; needs ce), generic (the "
                          "generic chunked linear loss; needs linear), fp16 (the ce and linear "
-                         "legs' workloads in fp16), small (the two smaller workloads, not in "
-                         "the default)")
+                         "legs' workloads in fp16), small (the two GPT-2-shaped workloads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--weight-steps", type=int, default=3)
     args = ap.parse_args()
@@ -157,17 +192,22 @@ def main() -> int:
         lin_out = [torch.empty((), dtype=torch.float32, device=dev),
                    torch.empty((), dtype=torch.int64, device=dev),
                    torch.empty((), dtype=torch.int32, device=dev)]
-        ws_bytes = max(_lib.linear_ce_workspace_bytes(lin_w.BT, lin_w.D, lin_w.V, _lib.LMX_BF16,
-                                                      lin_w.chunk_size, acc)
-                       for acc in (_lib.LMX_ACC_F32, _lib.LMX_ACC_WEIGHT))
+        one_group = gt_group_bytes_all(lin_w.BT, lin_w.V, lin_w.chunk_size)
+
+        def lin_ws_bytes(accum, group_bytes=0):
+            return _lib.linear_ce_workspace_bytes(lin_w.BT, lin_w.D, lin_w.V, _lib.LMX_BF16,
+                                                  lin_w.chunk_size, accum, group_bytes)
+        ws_bytes = max(lin_ws_bytes(_lib.LMX_ACC_F32), lin_ws_bytes(_lib.LMX_ACC_WEIGHT),
+                       lin_ws_bytes(_lib.LMX_ACC_F32, one_group))
         lin_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-        def lin_call(accum):
+        def lin_call(accum, group_bytes=0):
             st = _lib.linear_ce(X.data_ptr(), Wt.data_ptr(), tl.data_ptr(), lin_w.BT, lin_w.D,
                                 lin_w.V, _lib.LMX_BF16, -100, _lib.LMX_MEAN, lin_w.z_loss,
-                                lin_w.chunk_size, accum, lin_out[0].data_ptr(), gx.data_ptr(),
-                                gw.data_ptr(), lin_out[1].data_ptr(), lin_out[2].data_ptr(),
-                                lin_ws.data_ptr(), lin_ws.numel(), stream.cuda_stream)
+                                lin_w.chunk_size, accum, group_bytes, lin_out[0].data_ptr(),
+                                gx.data_ptr(), gw.data_ptr(), lin_out[1].data_ptr(),
+                                lin_out[2].data_ptr(), lin_ws.data_ptr(), lin_ws.numel(),
+                                stream.cuda_stream)
             _lib.check("linear_ce", st)
 
     # ------------------------------------------------------------ timed steps
@@ -193,7 +233,7 @@ def main() -> int:
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         wall_ms += (time.perf_counter() - t0) * 1e3 / K
-        ce_ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(K)) / K
+        ce_ms, ce_med = mean_median([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
     if "linear" in legs:
         for _ in range(W):
             lin_call(_lib.LMX_ACC_F32)
@@ -206,7 +246,7 @@ def main() -> int:
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         wall_ms += (time.perf_counter() - t0) * 1e3 / K
-        lin_ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(K)) / K
+        lin_ms, lin_med = mean_median([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
     log(f"step {wall_ms:.3f} ms (ce {ce_ms:.3f} ms, linear {lin_ms:.3f} ms)")
 
     line = {
@@ -228,7 +268,7 @@ def main() -> int:
                             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                             "traffic": traffic,
                             "algorithmic_bytes_per_launch": ce_bytes,
-                            "ms_per_launch": round(ce_ms, 4),
+                            "ms_per_launch": round(ce_ms, 4), "ms_median": round(ce_med, 4),
                             "kernel": "ce_rows_reg_kernel<bf16,1024,16> (+ count, finish)"}
         workload_names.append(ce_w.name)
         line["config"].update({"ce_B": ce_w.B, "ce_V": ce_w.V, "ce_reduction": "sum",
@@ -249,25 +289,27 @@ def main() -> int:
             if "clock_ghz_under_load" in mv:
                 mfma_busy["clock_ghz"] = float(mv["clock_ghz_under_load"])
         lin = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(lin_ms, 3),
+               "ms_median": round(lin_med, 3),
+               "workspace_bytes": lin_ws_bytes(_lib.LMX_ACC_F32),
                "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": lin_traffic,
                             "algorithmic_flops_per_call": flops,
                             "mfma_busy": mfma_busy,
                             "kernel": "whole linear_ce call (gemm_nt_kernel x3 per chunk + CE)"}}
-        # 'weight' accumulation, timed on its own
+        # 'weight' accumulation, and both modes with one grad_weight product over
+        # every chunk (a G^T budget that holds them all: more workspace, no
+        # fp32 accumulator), each timed on its own
         if args.weight_steps > 0:
-            lin_call(_lib.LMX_ACC_WEIGHT)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(args.weight_steps):
-                lin_call(_lib.LMX_ACC_WEIGHT)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wms = e0.elapsed_time(e1) / args.weight_steps
-            lin["weight_accum"] = {"value": round(flops / (wms * 1e-3) / 1e12, 1),
-                                   "unit": "TFLOP/s", "ms_per_call": round(wms, 3)}
+            for key, accum, gb in (("weight_accum", _lib.LMX_ACC_WEIGHT, 0),
+                                   ("one_group", _lib.LMX_ACC_F32, one_group),
+                                   ("weight_accum_one_group", _lib.LMX_ACC_WEIGHT, one_group)):
+                wms, wmed = mean_median(per_call_ms(lambda: lin_call(accum, gb),
+                                                    args.weight_steps, 1, stream))
+                lin[key] = {"value": round(flops / (wms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                            "ms_per_call": round(wms, 3), "ms_median": round(wmed, 3),
+                            "group_bytes": gb, "workspace_bytes": lin_ws_bytes(accum, gb)}
+                log(f"linear-CE {key}: {wms:.3f} ms")
         # the generic chunked loss with the library's cross-entropy as the caller's
         # loss (sum reduction, fp32 accumulation), on the same inputs
         if "generic" in legs:
@@ -417,7 +459,7 @@ def main() -> int:
                 _lib.check("linear_ce", _lib.linear_ce(
                     X16.data_ptr(), W16.data_ptr(), tl.data_ptr(), lin_w.BT, lin_w.D, lin_w.V,
                     _lib.LMX_F16, -100, _lib.LMX_MEAN, lin_w.z_loss, lin_w.chunk_size,
-                    _lib.LMX_ACC_F32, lin_out[0].data_ptr(), gx16.data_ptr(), gw16.data_ptr(),
+                    _lib.LMX_ACC_F32, 0, lin_out[0].data_ptr(), gx16.data_ptr(), gw16.data_ptr(),
                     lin_out[1].data_ptr(), lin_out[2].data_ptr(), lin_ws.data_ptr(),
                     lin_ws.numel(), stream.cuda_stream))
             lin16()
@@ -438,23 +480,29 @@ def main() -> int:
             del X16, W16, gx16, gw16
         line["fp16"] = f16
 
-    # ------------------------------------------------------------ smaller workloads
-    # the two smaller workloads (parity cases of the tests, not bench lines),
-    # timed only when asked for: CE [4096, 50257] bf16, mean, z 1e-4, out of
-    # place, and linear-CE [8192, 768] x [50257, 768], chunk 1024, fp32 accumulation
+    # ------------------------------------------------------------ GPT-2-shaped workloads
+    # the two smaller workloads, shaped after GPT-2's tied 50257 x 768 head:
+    # CE [4096, 50257] bf16, mean, z 1e-4, out of place (four copies of the
+    # logits in rotation, so that a call does not find its input in the 256 MB
+    # MALL from the call before), and linear-CE [8192, 768] x [50257, 768],
+    # chunk 1024, fp32 accumulation
     if "small" in legs:
         sm = {}
         cw = workloads.CE_B4096_V50257_BF16
         xh, th = workloads.ce_inputs(cw)
-        x2, t2 = xh.to(dev), th.to(dev)
-        g2 = torch.empty_like(x2)
+        t2 = th.to(dev)
+        xs = [xh.to(dev) for _ in range(4)]
+        g2 = torch.empty_like(xs[0])
         ws2 = torch.empty(_lib.ce_workspace_bytes(cw.B, cw.V, _lib.LMX_BF16), dtype=torch.uint8,
                           device=dev)
         o2 = [torch.empty((), dtype=torch.float32, device=dev),
               torch.empty((), dtype=torch.int64, device=dev),
               torch.empty((), dtype=torch.int32, device=dev)]
+        rot = [0]
 
         def ce2():
+            x2 = xs[rot[0] % len(xs)]
+            rot[0] += 1
             _lib.check("ce_fwd_bwd", _lib.ce_fwd_bwd(
                 x2.data_ptr(), g2.data_ptr(), t2.data_ptr(), cw.B, cw.V, _lib.LMX_BF16, -100,
                 _lib.LMX_MEAN, cw.z_loss[0], o2[0].data_ptr(), o2[1].data_ptr(), o2[2].data_ptr(),
@@ -463,42 +511,41 @@ def main() -> int:
         Xh, Wh, tlh = workloads.linear_ce_inputs(lw)
         X4, W4, t4 = Xh.to(dev), Wh.to(dev), tlh.to(dev)
         gx4, gw4 = torch.empty_like(X4), torch.empty_like(W4)
-        ws4 = torch.empty(_lib.linear_ce_workspace_bytes(lw.BT, lw.D, lw.V, _lib.LMX_BF16,
-                                                         lw.chunk_size, _lib.LMX_ACC_F32),
-                          dtype=torch.uint8, device=dev)
+        ws4_bytes = _lib.linear_ce_workspace_bytes(lw.BT, lw.D, lw.V, _lib.LMX_BF16,
+                                                   lw.chunk_size, _lib.LMX_ACC_F32, 0)
+        ws4 = torch.empty(ws4_bytes, dtype=torch.uint8, device=dev)
 
         def lin4():
             _lib.check("linear_ce", _lib.linear_ce(
                 X4.data_ptr(), W4.data_ptr(), t4.data_ptr(), lw.BT, lw.D, lw.V, _lib.LMX_BF16,
-                -100, _lib.LMX_MEAN, lw.z_loss, lw.chunk_size, _lib.LMX_ACC_F32,
+                -100, _lib.LMX_MEAN, lw.z_loss, lw.chunk_size, _lib.LMX_ACC_F32, 0,
                 o2[0].data_ptr(), gx4.data_ptr(), gw4.data_ptr(), o2[1].data_ptr(),
                 o2[2].data_ptr(), ws4.data_ptr(), ws4.numel(), stream.cuda_stream))
 
-        def timed(fn, n):
-            for _ in range(3):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(n):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / n
-        ms = timed(ce2, 20)
+        ms, med = mean_median(per_call_ms(ce2, 20, 4, stream))
         nbytes = 2 * cw.B * cw.V * 2 + 8 * cw.B
         gbps = nbytes / (ms * 1e-3) / 1e9
         sm[cw.name] = {"value": round(gbps, 1), "unit": "GB/s", "ms_per_call": round(ms, 4),
-                       "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+                       "ms_median": round(med, 4), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                       "algorithmic_bytes": nbytes,
+                       "traffic": stored_traffic("ce_rows_b4096_v50257_bf16.counters.txt",
+                                                 source_digest("ce.hip", "common.h")),
+                       "kernel": "ce_rows_reg_kernel<bf16,512,13> (+ count, finish)"}
         log(f"{cw.name}: {ms * 1e3:.1f} us, {gbps:.0f} GB/s")
-        ms = timed(lin4, 20)
+        ms, med = mean_median(per_call_ms(lin4, 20, 3, stream))
         flops = 6.0 * lw.BT * lw.V * lw.D
         tf = flops / (ms * 1e-3) / 1e12
         sm[lw.name] = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(ms, 4),
-                       "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+                       "ms_median": round(med, 4), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "algorithmic_flops": flops, "workspace_bytes": ws4_bytes,
+                       "traffic": stored_traffic(
+                           "linear_ce_bt8192_d768_v50257_c1024.counters.txt",
+                           source_digest("gemm.h", "linear_ce.hip", "ce.hip", "common.h"),
+                           "hbm_bytes_per_call"),
+                       "kernel": "whole linear_ce call"}
         log(f"{lw.name}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
         line["small_workloads"] = sm
-        del x2, g2, X4, W4, gx4, gw4
+        del xs, g2, X4, W4, gx4, gw4
 
     # ------------------------------------------------------------ oracle on the host
     if not args.no_cpu and "ce" in legs:

@@ -185,26 +185,37 @@ LMX_API int ce_fwd_bwd_noalloc(const void* logits, void* grad_logits, const int6
  *   accum         LMX_ACC_F32: grad_weight is accumulated in fp32 (within a
  *                 product over a group of chunks, and across groups in an fp32
  *                 workspace) and rounded once; LMX_ACC_WEIGHT: it is
- *                 accumulated in grad_weight itself, rounding after each chunk.
+ *                 accumulated in the weight's 16-bit format, rounding after
+ *                 each chunk (within a group's product, and from one group to
+ *                 the next through grad_weight itself).
+ *   group_bytes   the most workspace bytes that the transposed logits
+ *                 gradient of one grad_weight product may take: that product
+ *                 covers as many chunks as that holds (at least one), and one
+ *                 group's transposed gradient is all the workspace keeps of
+ *                 it, whatever BT. 0 selects the default, 2 GiB. A larger
+ *                 budget means fewer grad_weight passes (in fp32 mode, none
+ *                 over an fp32 accumulator once one group takes every chunk)
+ *                 for more workspace; < 0 is LMX_ERR_SIZE.
  *   loss          one fp32 on the device.
  *   grad_inputs   [BT, D] 16-bit output, 16-byte aligned.
  *   grad_weight   [V, D]  16-bit output, 16-byte aligned.
  *   n_valid, bad_target as for ce_fwd_bwd (may be NULL).
- *   workspace     >= linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum);
+ *   workspace     >= linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum,
+ *                 group_bytes);
  *                 its contents on entry do not matter.
  * Outputs must not overlap the inputs (LMX_ERR_ALIAS).
  */
 LMX_API int linear_ce(const void* inputs, const void* weight, const int64_t* target,
               int64_t BT, int64_t D, int64_t V, int dtype,
               int64_t ignore_index, int reduction, float z_loss_multiplier,
-              int64_t chunk_size, int accum,
+              int64_t chunk_size, int accum, int64_t group_bytes,
               float* loss, void* grad_inputs, void* grad_weight,
               int64_t* n_valid, int32_t* bad_target,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes linear_ce needs (0 for invalid arguments). */
 LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
-                                 int64_t chunk_size, int accum);
+                                 int64_t chunk_size, int accum, int64_t group_bytes);
 
 /*
  * linear_loss_logits -- logits of one row chunk for the generic chunked loss.

@@ -39,8 +39,8 @@ _SIGNATURES = {
     "ce_fwd_bwd_noalloc": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i64, _i32, _f32,
                                   _vp, _vp, _vp, _vp]),
     "linear_ce": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _f32,
-                         _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "linear_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32]),
+                         _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "linear_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i64, _i32, _i64]),
     "linear_ce_chunk_rows": (_i64, [_i64, _i64, _i64]),
     "lmx_status_string": (ctypes.c_char_p, [_i32]),
     "lmx_copy": (_i32, [_vp, _vp, _sz, _vp]),
@@ -117,16 +117,16 @@ def ce_workspace_bytes(B, V, dtype) -> int:
 
 
 def linear_ce(inputs, weight, target, BT, D, V, dtype, ignore_index, reduction,
-              z_loss_multiplier, chunk_size, accum, loss, grad_inputs, grad_weight,
+              z_loss_multiplier, chunk_size, accum, group_bytes, loss, grad_inputs, grad_weight,
               n_valid, bad_target, workspace, workspace_bytes, stream) -> int:
     return load().linear_ce(inputs, weight, target, BT, D, V, dtype, ignore_index, reduction,
-                            z_loss_multiplier, chunk_size, accum, loss, grad_inputs,
+                            z_loss_multiplier, chunk_size, accum, group_bytes, loss, grad_inputs,
                             grad_weight, n_valid, bad_target, workspace, workspace_bytes,
                             stream)
 
 
-def linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum) -> int:
-    return load().linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum)
+def linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum, group_bytes) -> int:
+    return load().linear_ce_workspace_bytes(BT, D, V, dtype, chunk_size, accum, group_bytes)
 
 
 def linear_ce_chunk_rows(BT, V, chunk_size) -> int:

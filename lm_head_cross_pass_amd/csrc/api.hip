@@ -226,7 +226,7 @@ size_t linear_loss_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
   if (V > kLinMaxV || D > kLinMaxD) return 0;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
   if (c > kLinMaxChunk) return 0;
-  return lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true).total;
+  return lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true, 0).total;
 }
 
 int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, int64_t D,
@@ -289,7 +289,7 @@ int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad
       overlaps(grad_weight, wb, weight, wb) || overlaps(grad_weight, wb, grad_logits, gb) ||
       overlaps(grad_inputs_c, xb, grad_weight, wb))
     return LMX_ERR_ALIAS;
-  const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true);
+  const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true, 0);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
   lmx::LinearLossChunk p{};
   p.dtype = dtype;
@@ -315,26 +315,27 @@ int64_t linear_ce_chunk_rows(int64_t BT, int64_t V, int64_t chunk_size) {
 }
 
 size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
-                                 int64_t chunk_size, int accum) {
-  if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0) return 0;
+                                 int64_t chunk_size, int accum, int64_t group_bytes) {
+  if (BT < 0 || D <= 0 || V <= 0 || chunk_size < 0 || group_bytes < 0) return 0;
   if (dtype != LMX_BF16 && dtype != LMX_F16) return 0;
   if (accum != LMX_ACC_F32 && accum != LMX_ACC_WEIGHT) return 0;
   if (V > kLinMaxV || D > kLinMaxD) return 0;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
   if (c > kLinMaxChunk) return 0;
-  return lmx::linear_ce_workspace_layout(BT, D, V, c, accum).total;
+  return lmx::linear_ce_workspace_layout(BT, D, V, c, accum, false, group_bytes).total;
 }
 
 int linear_ce(const void* inputs, const void* weight, const int64_t* target, int64_t BT,
               int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction,
-              float z_loss_multiplier, int64_t chunk_size, int accum, float* loss,
-              void* grad_inputs, void* grad_weight, int64_t* n_valid, int32_t* bad_target,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              float z_loss_multiplier, int64_t chunk_size, int accum, int64_t group_bytes,
+              float* loss, void* grad_inputs, void* grad_weight, int64_t* n_valid,
+              int32_t* bad_target, void* workspace, size_t workspace_bytes, void* stream) {
   if (weight == nullptr || loss == nullptr || grad_weight == nullptr || workspace == nullptr)
     return LMX_ERR_NULL;
   if (BT > 0 && (inputs == nullptr || target == nullptr || grad_inputs == nullptr))
     return LMX_ERR_NULL;
-  if (BT < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD) return LMX_ERR_SIZE;
+  if (BT < 0 || D <= 0 || V <= 0 || V > kLinMaxV || D > kLinMaxD || group_bytes < 0)
+    return LMX_ERR_SIZE;
   if (chunk_size < 0) return LMX_ERR_CHUNK;
   if (!dtype_ok(dtype)) return LMX_ERR_ENUM;
   if (reduction != LMX_MEAN && reduction != LMX_SUM) return LMX_ERR_ENUM;
@@ -356,7 +357,8 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
     return LMX_ERR_ALIAS;
   const int64_t c = lmx::linear_ce_resolve_chunk(BT, V, chunk_size);
   if (c > kLinMaxChunk) return LMX_ERR_SIZE;
-  const lmx::LinearCeWorkspace wl = lmx::linear_ce_workspace_layout(BT, D, V, c, accum);
+  const lmx::LinearCeWorkspace wl =
+      lmx::linear_ce_workspace_layout(BT, D, V, c, accum, false, group_bytes);
   if (workspace_bytes < wl.total) return LMX_ERR_WORKSPACE;
   lmx::LinearCeParams p{};
   p.dtype = dtype;
@@ -371,6 +373,7 @@ int linear_ce(const void* inputs, const void* weight, const int64_t* target, int
   p.reduction = reduction;
   p.chunk = c;
   p.accum = accum;
+  p.group_bytes = group_bytes;
   p.loss = loss;
   p.grad_x = static_cast<uint16_t*>(grad_inputs);
   p.grad_w = static_cast<uint16_t*>(grad_weight);

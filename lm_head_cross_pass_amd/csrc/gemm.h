@@ -32,7 +32,9 @@
 //   contiguous range of tiles (tiles that share A or B panels share an L2),
 //   whatever the grid size.
 //
-// The epilogue is a functor called with the accumulators (see linear_ce.hip).
+// The epilogue is a functor (see linear_ce.hip): init() sets the accumulators
+// before the K loop, run() stores them after it, and an epilogue with kRounds
+// also rounds them every round_every K steps (round()).
 #pragma once
 
 #include "common.h"
@@ -94,6 +96,10 @@ struct GemmShape {
   uint16_t* bt_out;
   int64_t ld_bt;
   int bt_cols;
+  // K steps between two roundings of the accumulators by the epilogue (its
+  // round(); only epilogues with kRounds), 0 for none: the weight-dtype
+  // accumulation of grad_weight, one rounding per chunk of the K range.
+  int round_every;
 };
 
 // Block tile BM x BN: 2 x 2 waves for 128 x 128, 2 x 4 waves for 256 x 256;
@@ -119,6 +125,17 @@ struct GemmCfg {
   static constexpr int B_LOADS = BN / ROWS_PER_COPY / NWAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS;
 };
+
+// Accumulators set to zero (the init() of most epilogues).
+template <int FM, int FN>
+__device__ __forceinline__ void acc_zero(f32x16_t (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
 
 // Slot swizzle of an LDS row of CPR 16-byte chunks (CPR = 4 or 8): 8 or 16
 // consecutive rows reading the same logical chunk hit distinct bank groups.
@@ -373,13 +390,10 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     b_voff[i] = static_cast<int>((static_cast<int64_t>(r) * g.ldb + b_kc[i]) * 2);
   }
 
+  // accumulators: zero, or a starting value the epilogue loads
+  const AccCoord ac{wm * C::WM, wn * C::WN, lane};
   f32x16_t acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  epi.template init<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, g);
 
   // Fragment reads: lane l reads 16 bytes of row (l & 31) of each 32-row MFMA
   // tile, k chunk 2 kk + (l >> 5); the byte offset of slice kk is the slice-0
@@ -437,6 +451,11 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
       gemm_interleave_hint<C, SCHED>();
     }
     gemm_mfma_slice<C, E>(acc, fa1, fb1);
+    if constexpr (Epi::kRounds) {
+      // a chunk boundary inside the K range: the epilogue rounds the running
+      // sums (the last boundary is the epilogue's own rounding)
+      if (g.round_every > 0 && (ks + 1) % g.round_every == 0 && ks + 1 < ke) epi.round(acc);
+    }
     if (g.at_out != nullptr && ks % g.tiles_n == tn) {
       gemm_store_tile_transposed<C, BM>(smem + cur_bytes, g.at_out, g.ld_at, m0, g.at_cols,
                                         ks * kGemmBK, g.K);
@@ -454,7 +473,6 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
       gemm_load_frags<C, 0>(smem, a_off, b_off, nxt_bytes, fa0, fb0);
     }
   }
-  AccCoord ac{wm * C::WM, wn * C::WN, lane};
   epi.template run<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, split, g,
                                          reinterpret_cast<uint16_t*>(smem));
 }

@@ -76,6 +76,7 @@ struct LinearCeParams {
   int reduction;
   int64_t chunk;            // rows per chunk (resolved, > 0)
   int accum;                // LMX_ACC_F32 / LMX_ACC_WEIGHT
+  int64_t group_bytes;      // G^T budget of one grad_weight product (0: the default)
   float* loss;
   uint16_t* grad_x;         // [BT, D]
   uint16_t* grad_w;         // [V, D]
@@ -87,15 +88,16 @@ struct LinearCeWorkspace {
   int64_t ldv;              // padded vocabulary stride of the chunk buffers
   int64_t ldc;              // padded chunk-row stride of the transposed buffers
   int64_t ksplit;           // K splits of the grad_inputs GEMM
-  int64_t dw_group;         // chunks per grad_weight product (fp32 mode: as many as 2 GiB of G^T holds; else 1)
+  int64_t dw_group;         // chunks per grad_weight product (as many as the G^T budget holds)
   int64_t ldk;              // row stride of G^T and X_c^T: dw_group * ldc
   size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, dxp_off, dw_off, dwp_off, total;
   size_t dwp_bytes;         // K-split partials of grad_weight's last rows (0: none)
 };
 // generic = true: the layout of the generic chunked loss (no chunk logits
-// buffer: the caller holds them; one grad_weight product per chunk).
+// buffer: the caller holds them). group_bytes: the G^T budget of one
+// grad_weight product (0: the default, 2 GiB).
 LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, int64_t chunk,
-                                             int accum, bool generic = false);
+                                             int accum, bool generic, int64_t group_bytes);
 int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size);
 int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream);
 

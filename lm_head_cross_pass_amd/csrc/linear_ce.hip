@@ -74,6 +74,7 @@ inline int staged_ok(const void* out, int64_t ld, int64_t n) {
 
 template <typename E>
 struct EpiOut {
+  static constexpr bool kRounds = false;
   uint16_t* out;
   int64_t ldo;
   float* partial;        // [ksplit][M][ldp]
@@ -91,6 +92,13 @@ struct EpiOut {
     e.out = out + rows * ldo + cols;
     return e;
   }
+
+  template <int BM, int BN, int FM, int FN>
+  __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord&, int, int, const GemmShape&) {
+    acc_zero(acc);
+  }
+  template <int FM, int FN>
+  __device__ void round(f32x16_t (&)[FM][FN]) {}
 
   // Staged path: the tile in LDS as [BM][BN] 16-bit values, the 16-byte pieces
   // of a row XOR-swizzled by bit 2 of (row >> 2), which sends the two halves of
@@ -163,13 +171,15 @@ struct EpiOut {
 };
 
 // grad_weight epilogue modes; "W16" is the weight's 16-bit format (bf16 / fp16).
-enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToW16 = 2, kDwStoreW16 = 3, kDwAddW16 = 4 };
+// ('weight' accumulation has its own epilogue, EpiDwW16.)
+enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToW16 = 2, kDwStoreW16 = 3 };
 
 // Step 6: grad_weight accumulation. Read-modify-write epilogues issue all the
 // reads of an accumulator column before any add, so the memory latency is paid
 // once per column (this measured faster than fire-and-forget buffer atomics).
 template <typename E>
 struct EpiDw {
+  static constexpr bool kRounds = false;
   float* acc32;     // [V][ld] fp32 accumulator ('fp32' mode)
   uint16_t* out16;  // [V][ld] grad_weight in the weight's format E
   int64_t ld;
@@ -184,6 +194,13 @@ struct EpiDw {
     return e;
   }
 
+  template <int BM, int BN, int FM, int FN>
+  __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord&, int, int, const GemmShape&) {
+    acc_zero(acc);
+  }
+  template <int FM, int FN>
+  __device__ void round(f32x16_t (&)[FM][FN]) {}
+
   template <int MODE, int FM, int FN>
   __device__ void apply(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int n0, const GemmShape& g,
                         __amdgpu_buffer_rsrc_t r32, __amdgpu_buffer_rsrc_t r16, float s) {
@@ -192,7 +209,7 @@ struct EpiDw {
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + ac.col(j);
       if (col >= g.N) continue;
-      if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToW16 || MODE == kDwAddW16) {
+      if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToW16) {
         // read-modify-write: all FM x 16 reads of this column first, so their
         // latency is paid once per column instead of once per element
         float old[FM * 16];
@@ -201,11 +218,7 @@ struct EpiDw {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int e = ac.row(i, r) * ldi + col;
-            if constexpr (MODE == kDwAddF32 || MODE == kDwAddF32ToW16) {
-              old[i * 16 + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r32, e * 4, 0, 0));
-            } else {
-              old[i * 16 + r] = E::widen(__builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0));
-            }
+            old[i * 16 + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r32, e * 4, 0, 0));
           }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -246,8 +259,109 @@ struct EpiDw {
       case kDwStoreF32: apply<kDwStoreF32>(acc, ac, n0, g, r32, r16, s); break;
       case kDwAddF32: apply<kDwAddF32>(acc, ac, n0, g, r32, r16, s); break;
       case kDwAddF32ToW16: apply<kDwAddF32ToW16>(acc, ac, n0, g, r32, r16, s); break;
-      case kDwStoreW16: apply<kDwStoreW16>(acc, ac, n0, g, r32, r16, s); break;
-      default: apply<kDwAddW16>(acc, ac, n0, g, r32, r16, s); break;
+      default: apply<kDwStoreW16>(acc, ac, n0, g, r32, r16, s); break;
+    }
+  }
+};
+
+// Step 6 in 'weight' accumulation: grad_weight in the weight's 16-bit format E,
+// rounded after every chunk, for a product over a group of chunks (K = the
+// group's chunk columns of G^T / X^T, round_every K steps per chunk). The
+// accumulators hold dW_prev / s + P (s = 1 / N for the mean, 1 for the sum;
+// P the fp32 product of the chunks so far in the group), so that at each chunk
+// boundary dW = E(s acc) is the running gradient rounded to E, and acc restarts
+// from dW / s: the product is the chunk-by-chunk RNE(dW + s P_c), with one
+// product per group instead of one per chunk. The first group starts from
+// zero; a later group loads the running gradient from grad_weight (preload).
+// 1 / s = N is exact in fp32 for N < 2^24, and dW N is exact whenever E's
+// significand and N fit 24 bits together (bf16 and N < 2^16).
+template <typename E>
+struct EpiDwW16 {
+  static constexpr bool kRounds = true;
+  uint16_t* out16;  // [V][ld] grad_weight in E
+  int64_t ld;
+  const int64_t* mean_count;   // non-null: the mean's N
+  int preload;                 // start from the gradient in out16 (a later group)
+
+  EpiDwW16 shifted(int64_t rows, int64_t cols) const {
+    EpiDwW16 e = *this;
+    e.out16 = out16 + rows * ld + cols;
+    return e;
+  }
+
+  __device__ static float count_f(const int64_t* n) {
+    if (n == nullptr) return 1.0f;
+    const int64_t v = *n;
+    return v > 0 ? static_cast<float>(v) : 1.0f;
+  }
+
+  template <int BM, int BN, int FM, int FN>
+  __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0,
+                       const GemmShape& g) {
+    if (!preload) {
+      acc_zero(acc);
+      return;
+    }
+    const float nf = count_f(mean_count);
+    const __amdgpu_buffer_rsrc_t r16 = rows_rsrc(out16, m0, g.M - m0, BM, ld * 2);
+    const int ldi = static_cast<int>(ld);
+    // every load is issued before any value is used (the raw 16 bits go into
+    // the accumulator registers), so the tile pays the memory latency once;
+    // rows past M lie outside the resource and read zero, and the columns past
+    // N (whose offsets may reach into the next row) are zeroed below
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + ac.col(j);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = ac.row(i, r) * ldi + col;
+          acc[i][j][r] = __uint_as_float(static_cast<uint32_t>(
+              __builtin_amdgcn_raw_buffer_load_b16(r16, e * 2, 0, 0)));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float keep = n0 + ac.col(j) < g.N ? nf : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint16_t bits = static_cast<uint16_t>(__float_as_uint(acc[i][j][r]));
+          acc[i][j][r] = E::widen(bits) * keep;
+        }
+    }
+  }
+
+  template <int FM, int FN>
+  __device__ void round(f32x16_t (&acc)[FM][FN]) {
+    const float s = count_scale(mean_count), nf = count_f(mean_count);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = E::widen(E::narrow(s * acc[i][j][r])) * nf;
+  }
+
+  template <int BM, int BN, int FM, int FN>
+  __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int,
+                      const GemmShape& g, uint16_t*) {
+    const __amdgpu_buffer_rsrc_t r16 = rows_rsrc(out16, m0, g.M - m0, BM, ld * 2);
+    const float s = count_scale(mean_count);
+    const int ldi = static_cast<int>(ld);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + ac.col(j);
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = ac.row(i, r) * ldi + col;   // rows >= M are dropped
+          __builtin_amdgcn_raw_buffer_store_b16(E::narrow(s * acc[i][j][r]), r16, e * 2, 0, 0);
+        }
     }
   }
 };
@@ -337,8 +451,7 @@ __global__ __launch_bounds__(256) void dw_tail_reduce_kernel(const float* __rest
     case kDwStoreF32: acc32[e] = v; break;
     case kDwAddF32: acc32[e] = acc32[e] + v; break;
     case kDwAddF32ToW16: out16[e] = E::narrow(acc32[e] + v); break;
-    case kDwStoreW16: out16[e] = E::narrow(v); break;
-    default: out16[e] = E::narrow(E::widen(out16[e]) + v); break;
+    default: out16[e] = E::narrow(v); break;
   }
 }
 
@@ -457,6 +570,7 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.bt_out = nullptr;
   g.ld_bt = 0;
   g.bt_cols = 0;
+  g.round_every = 0;
   return g;
 }
 
@@ -592,6 +706,46 @@ int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int
                         : launch_gemm<1, E>(gs, tile, e, stream);
 }
 
+// grad_weight product in 'weight' accumulation over the K = ngroup_chunks *
+// ldc columns of a group: rounded to E after every chunk (round_every K steps
+// per chunk), starting from zero (the first group) or from the running
+// gradient in gw (preload, a later group). No K-split tail: the rounding
+// needs the chunks in order within one workgroup, so a ragged last wave goes
+// to small tiles instead.
+template <typename E>
+int grad_weight_product_w16(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int K, int V,
+                            int D, uint16_t* gw, int64_t ldw, const int64_t* mean_count,
+                            int round_every, bool preload, hipStream_t stream) {
+  const int tile = pick_tile(V, D);
+  GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
+  gs.round_every = round_every;
+  EpiDwW16<E> e{gw, ldw, mean_count, preload ? 1 : 0};
+  return tile == kTileL ? launch_gemm_split_tail<1, E>(gs, e, stream)
+                        : launch_gemm<1, E>(gs, tile, e, stream);
+}
+
+// The grad_weight product of group gi (of ngroups) over its chunk columns:
+// fp32 accumulation (store / read-modify-write of the fp32 workspace, the
+// last group rounding to E; one group writes E directly) or the weight
+// dtype's per-chunk rounding.
+template <typename E>
+int grad_weight_group(int accum, int64_t gi, int64_t ngroups, const uint16_t* gt,
+                      const uint16_t* xt, int64_t ldk, int K, int64_t ldc, int V, int D,
+                      float* dw, uint16_t* gw, int64_t ldw, const int64_t* mean_count,
+                      float* tailp, size_t tail_bytes, hipStream_t stream) {
+  if (accum == LMX_ACC_WEIGHT) {
+    return grad_weight_product_w16<E>(gt, xt, ldk, K, V, D, gw, ldw, mean_count,
+                                      static_cast<int>(ldc / kGemmBK), gi > 0, stream);
+  }
+  const bool first = gi == 0, last = gi == ngroups - 1;
+  const int mode = ngroups == 1 ? kDwStoreW16
+                   : first      ? kDwStoreF32
+                   : last       ? kDwAddF32ToW16
+                                : kDwAddF32;
+  return grad_weight_product<E>(gt, xt, ldk, K, V, D, dw, gw, ldw, mode, mean_count, tailp,
+                                tail_bytes, stream);
+}
+
 }  // namespace
 
 int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size) {
@@ -607,25 +761,24 @@ int64_t linear_ce_resolve_chunk(int64_t BT, int64_t V, int64_t chunk_size) {
 }
 
 LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, int64_t chunk,
-                                             int accum, bool generic) {
+                                             int accum, bool generic, int64_t group_bytes) {
   LinearCeWorkspace w{};
   const int64_t C = chunk > 0 ? chunk : 1;
   w.ldv = round_up64(V, kLdvAlign);
   w.ldc = round_up64(C, kLdcAlign);
   w.ksplit = dx_plan(C, D, w.ldv).ksplit;
   const int64_t nchunks = BT > 0 ? (BT + C - 1) / C : 0;
-  // fp32 accumulation takes the grad_weight product of several chunks at once
-  // (K = group ldc): as many chunks as G^T of 2 GiB holds, so the fp32
-  // accumulator is read and written once per group instead of once per chunk
-  // (in the fused and the generic path alike)
+  // grad_weight is taken once per group of chunks (K = the group's chunk
+  // columns of G^T and X^T): as many chunks as group_bytes of G^T hold, at
+  // least one. In fp32 mode a group's product reads and writes the fp32
+  // accumulator once instead of once per chunk (none is kept when one group
+  // takes every chunk); in weight-dtype mode the product rounds after each of
+  // its chunks. The budget bounds the workspace whatever BT is.
+  const int64_t budget = group_bytes > 0 ? group_bytes : kGtGroupBytes;
   w.dw_group = 1;
-  if (accum == LMX_ACC_F32 && nchunks > 1) {
+  if (nchunks > 1) {
     const int64_t per_chunk = w.ldv * w.ldc * 2;
-    int64_t gsz = kGtGroupBytes / per_chunk;
-    // when G^T of every chunk fits in the group budget plus the fp32
-    // accumulator's bytes, one group takes them all: a single product over
-    // K = BT writes the rounded 16-bit grad_weight and no accumulator is kept
-    if (nchunks * per_chunk <= kGtGroupBytes + V * D * 4) gsz = nchunks;
+    int64_t gsz = budget / per_chunk;
     if (gsz > nchunks) gsz = nchunks;
     // the GEMM addresses 256 rows of G^T / X^T with 32-bit byte offsets
     const int64_t gmax = ((int64_t{1} << 31) - 1) / (256 * 2 * w.ldc);
@@ -648,8 +801,9 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
   w.dw_off = take(accum == LMX_ACC_F32 && nchunks > w.dw_group ? static_cast<size_t>(V) * D * 4
                                                                  : 0);
-  // K-split partials of grad_weight's last rows (the largest K any product has)
-  w.dwp_bytes = dw_tail_bytes(V, D, w.ldk);
+  // K-split partials of grad_weight's last rows (the largest K any product
+  // has; fp32 mode only)
+  w.dwp_bytes = accum == LMX_ACC_F32 ? dw_tail_bytes(V, D, w.ldk) : 0;
   w.dwp_off = take(w.dwp_bytes);
   w.total = off;
   return w;
@@ -657,7 +811,8 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
 
 template <typename E>
 int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
-  const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum);
+  const LinearCeWorkspace wl =
+      linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum, false, p.group_bytes);
   char* ws = static_cast<char*>(ws_base);
   int64_t* n_ws = reinterpret_cast<int64_t*>(ws + wl.n_valid_off);
   float* row_loss = reinterpret_cast<float*>(ws + wl.row_loss_off);
@@ -739,16 +894,9 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     if (st != LMX_OK) return st;
     // 6. grad_weight, once per group of chunks
     if (slot == grp - 1 || c == nchunks - 1) {
-      const int64_t gi = c / grp, ngroups = (nchunks + grp - 1) / grp;
-      const bool first = gi == 0, last = gi == ngroups - 1;
-      int mode;
-      if (p.accum == LMX_ACC_F32) {
-        mode = ngroups == 1 ? kDwStoreW16 : first ? kDwStoreF32 : last ? kDwAddF32ToW16 : kDwAddF32;
-      } else {
-        mode = first ? kDwStoreW16 : kDwAddW16;
-      }
-      st = grad_weight_product<E>(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw,
-                                  p.grad_w, p.D, mode, mean_count, dwp, wl.dwp_bytes, stream);
+      st = grad_weight_group<E>(p.accum, c / grp, (nchunks + grp - 1) / grp, gt, xt, ldk,
+                                static_cast<int>((slot + 1) * ldc), ldc, V, D, dw, p.grad_w, p.D,
+                                mean_count, dwp, wl.dwp_bytes, stream);
       if (st != LMX_OK) return st;
     }
   }
@@ -768,7 +916,7 @@ int linear_loss_logits_run(const uint16_t* xc, const uint16_t* w, int rows, int 
 
 template <typename E>
 int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t stream) {
-  const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum, true);
+  const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum, true, 0);
   char* ws = static_cast<char*>(ws_base);
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
   uint16_t* xt = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
@@ -801,16 +949,9 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   // grad_weight, once per group of chunks (the group's G^T and X^T columns
   // stay in the workspace between the calls)
   if (slot != grp - 1 && p.index != nchunks - 1) return LMX_OK;
-  const int64_t gi = p.index / grp, ngroups = (nchunks + grp - 1) / grp;
-  const bool first = gi == 0, last = gi == ngroups - 1;
-  int mode;
-  if (p.accum == LMX_ACC_F32) {
-    mode = ngroups == 1 ? kDwStoreW16 : first ? kDwStoreF32 : last ? kDwAddF32ToW16 : kDwAddF32;
-  } else {
-    mode = first ? kDwStoreW16 : kDwAddW16;
-  }
-  return grad_weight_product<E>(gt, xt, ldk, static_cast<int>((slot + 1) * ldc), V, D, dw,
-                                p.grad_w, p.D, mode, nullptr, dwp, wl.dwp_bytes, stream);
+  return grad_weight_group<E>(p.accum, p.index / grp, (nchunks + grp - 1) / grp, gt, xt, ldk,
+                              static_cast<int>((slot + 1) * ldc), ldc, V, D, dw, p.grad_w, p.D,
+                              nullptr, dwp, wl.dwp_bytes, stream);
 }
 
 int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream) {

@@ -148,8 +148,12 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
               ignore_index: int = -100, reduction: str = "mean",
               z_loss_multiplier: float = 0.0, chunk_size: Optional[int] = None,
               grad_weight_accum_dtype: str = "fp32",
-              workspace: Optional[torch.Tensor] = None):
-    """One library call: (loss, grad_inputs, grad_weight, n_valid, bad_target)."""
+              workspace: Optional[torch.Tensor] = None,
+              group_bytes: Optional[int] = None):
+    """One library call: (loss, grad_inputs, grad_weight, n_valid, bad_target).
+
+    ``group_bytes`` bounds the workspace bytes of transposed logits gradient
+    that one grad_weight product covers (None: the library's default, 2 GiB)."""
     for t, n in ((inputs, "inputs"), (weight, "weight")):
         _require_device(t, n)
         if t.dim() != 2 or not t.is_contiguous():
@@ -173,7 +177,10 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
     cs = 0 if chunk_size is None else int(chunk_size)
     acc = _ACCUMS[grad_weight_accum_dtype]
     ldt = _LINEAR_DTYPES[inputs.dtype]
-    nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, ldt, cs, acc)
+    gb = 0 if group_bytes is None else int(group_bytes)
+    if gb < 0:
+        raise ValueError("group_bytes must be >= 0")
+    nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, ldt, cs, acc, gb)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
@@ -184,7 +191,7 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
     with torch.cuda.device(dev):
         st = _lib.linear_ce(inputs.data_ptr(), weight.data_ptr(), target.data_ptr(), BT, D, V,
                             ldt, int(ignore_index), _REDUCTIONS[reduction],
-                            float(z_loss_multiplier), cs, acc, loss.data_ptr(), gx.data_ptr(),
+                            float(z_loss_multiplier), cs, acc, gb, loss.data_ptr(), gx.data_ptr(),
                             gw.data_ptr(), n_valid.data_ptr(), bad.data_ptr(),
                             workspace.data_ptr(), workspace.numel(), _stream_handle(dev))
     _lib.check("linear_ce", st)

@@ -76,12 +76,40 @@ def test_workspace_sizes():
     assert _lib.ce_workspace_bytes(4, 1 << 30, BF16) == 0
     assert _lib.ce_workspace_bytes(4, (1 << 29) - 8, F32) == 0
     assert _lib.ce_workspace_bytes(4, (1 << 29) - 8, BF16) > 0
-    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 0) > 0
-    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, F32, 1024, 0) == 0
-    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, -1, 0) == 0
-    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 5) == 0
-    assert _lib.linear_ce_workspace_bytes(8192, 768, 4194048 + 1, BF16, 1024, 0) == 0
-    assert _lib.linear_ce_workspace_bytes(8192, 2097088 + 8, 1000, BF16, 1024, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 0, 0) > 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, F32, 1024, 0, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, -1, 0, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 5, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 50257, BF16, 1024, 0, -1) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 768, 4194048 + 1, BF16, 1024, 0, 0) == 0
+    assert _lib.linear_ce_workspace_bytes(8192, 2097088 + 8, 1000, BF16, 1024, 0, 0) == 0
+
+
+def test_grad_weight_group_budget_bounds_the_workspace():
+    # inputs [BT, 4096] x weight [128256, 4096], chunks of 2048: G^T of one
+    # chunk is 128512 x 2048 bf16 (526 MB)
+    D, V, C = 4096, 128256, 2048
+    gt_chunk = 128512 * 2048 * 2
+    acc32 = V * D * 4
+
+    def ws(BT, accum, budget):
+        return _lib.linear_ce_workspace_bytes(BT, D, V, BF16, C, accum, budget)
+    # the default budget (2 GiB: four chunks per product) does not grow with BT
+    # beyond the per-row loss terms
+    base = ws(16384, 0, 0)
+    assert ws(65536, 0, 0) - base <= (65536 - 16384) * 4 + 256
+    # the default is the 2 GiB budget given explicitly
+    assert ws(16384, 0, 1 << 31) == base
+    xt_chunk = D * 2048 * 2
+    # fp32 mode: one product over all 8 chunks keeps no fp32 accumulator but
+    # holds 4 more chunks of G^T and X^T
+    one = ws(16384, 0, 8 * gt_chunk)
+    assert 4 * gt_chunk - acc32 < one - base <= 4 * (gt_chunk + xt_chunk) - acc32
+    # a budget of one chunk: 3 chunks less of G^T and X^T than the default
+    small = ws(16384, 0, gt_chunk)
+    assert 3 * gt_chunk <= base - small <= 3 * (gt_chunk + xt_chunk) + (64 << 20)
+    # weight-dtype mode keeps no fp32 accumulator
+    assert ws(16384, 1, 0) <= base - acc32
 
 
 def test_chunk_rows():
@@ -126,13 +154,13 @@ def test_ce_argument_errors(kw, status):
 
 def _lin(**kw):
     args = dict(x=A, w=A + (1 << 34), t=A + (2 << 34), BT=64, D=64, V=1000, dtype=BF16,
-                ignore=-100, red=MEAN, z=0.0, chunk=16, acc=0, loss=A + (3 << 34),
+                ignore=-100, red=MEAN, z=0.0, chunk=16, acc=0, gb=0, loss=A + (3 << 34),
                 gx=A + (5 << 34), gw=A + (6 << 34), n=None, bad=None, ws=A + (4 << 34),
                 wsb=1 << 40, stream=None)
     args.update(kw)
     return _lib.linear_ce(args["x"], args["w"], args["t"], args["BT"], args["D"], args["V"],
                           args["dtype"], args["ignore"], args["red"], args["z"], args["chunk"],
-                          args["acc"], args["loss"], args["gx"], args["gw"], args["n"],
+                          args["acc"], args["gb"], args["loss"], args["gx"], args["gw"], args["n"],
                           args["bad"], args["ws"], args["wsb"], args["stream"])
 
 
@@ -147,6 +175,7 @@ def _lin(**kw):
     (dict(D=2097088 + 8), _lib.LMX_ERR_SIZE),
     (dict(BT=5 << 20, chunk=4194240 + 64), _lib.LMX_ERR_SIZE),  # chunk > 4194240 rows
     (dict(chunk=-1), _lib.LMX_ERR_CHUNK),
+    (dict(gb=-1), _lib.LMX_ERR_SIZE),
     (dict(dtype=F32), _lib.LMX_ERR_UNSUPPORTED),
     (dict(dtype=3), _lib.LMX_ERR_ENUM),
     (dict(red=5), _lib.LMX_ERR_ENUM),

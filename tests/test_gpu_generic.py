@@ -160,8 +160,9 @@ def test_workspace_contents_do_not_matter_generic(accum):
 @pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
 def test_split_tail_launches_generic(dtype):
     # D = 768 and V = 50256: the chunk's logits product has 4 x 197 large tiles,
-    # so its last columns go to a second launch on small tiles; grad_weight
-    # likewise splits its last rows
+    # so its last columns go to a second launch on small tiles; grad_weight is
+    # one product over both chunks (K = 2048) whose last wave of rows runs as
+    # large tiles with K split in three, summed by the tail reduction
     BT, D, V = 2048, 768, 50256
     X, W, t = workloads.small_linear_ce(BT, D, V, dtype=dtype, n_ignored=30, seed=41)
     loss, gx, gw = F.chunked_linear_loss_fwd(X.to(DEV), W.to(DEV), F.cross_entropy_loss_and_grad,

@@ -179,7 +179,7 @@ def test_workspace_contents_do_not_matter(BT, D, V, chunk, accum):
     Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
     from lm_head_cross_pass_amd import _lib
     nbytes = _lib.linear_ce_workspace_bytes(BT, D, V, _lib.LMX_BF16, chunk,
-                                            0 if accum == "fp32" else 1)
+                                            0 if accum == "fp32" else 1, 0)
     outs = []
     for fill in (0x00, 0xFF):
         ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
@@ -202,9 +202,10 @@ def test_workload_bt8192_d768_v50257_full():
 
 
 def test_weight_accumulation_with_split_tail_launches():
-    # D = 768, V = 50257, two chunks of 1024 in 'weight' mode: each chunk's
-    # grad_weight product stores (then read-modify-writes) the bf16 gradient
-    # through a large-tile launch and a small-tile launch for its last rows
+    # D = 768, V = 50257, two chunks of 1024 in 'weight' mode: one grad_weight
+    # product over both chunks (K = 2048) rounds to bf16 after the first chunk
+    # inside its K loop; its large tiles leave a last wave under a third full,
+    # so the last rows go to a second launch on small tiles
     BT, D, V, C = 2048, 768, 50257, 1024
     X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=20, seed=47)
     emu = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, "weight", chunk_size=C,
@@ -409,3 +410,57 @@ def test_tiny_edges(BT, D, V, chunk, dtype):
 def olce_chunk(BT, V, chunk):
     from lm_head_cross_pass_amd import _lib
     return int(_lib.linear_ce_chunk_rows(BT, V, chunk))
+
+
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_grad_weight_groups_of_any_size(dtype):
+    """32 chunks of 16 rows, grad_weight taken over groups of 1, 3 (the last
+    group ragged) or all 32 chunks (the budget in bytes of G^T, 512 x 64 x 2 a
+    chunk). 'weight' mode rounds after every chunk inside a group's product and
+    carries the running bf16 gradient from group to group, so every grouping
+    gives the same bits, close to the chunk-by-chunk emulation; 'fp32' mode
+    stays within the bar of the exact value for every grouping; grad_inputs
+    does not depend on the grouping."""
+    BT, D, V, C = 512, 64, 300, 16
+    X, W, t = workloads.small_linear_ce(BT, D, V, dtype=dtype, n_ignored=10, seed=31)
+    Xd, Wd, td = X.to(DEV), W.to(DEV), t.to(DEV)
+    per_chunk = 512 * 64 * 2
+    budgets = (per_chunk, 3 * per_chunk, 0)
+    emu = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, "weight", chunk_size=C)
+    exact = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4)
+    outs = {acc: [F.linear_ce(Xd, Wd, td, -100, "mean", 1e-4, C, acc, group_bytes=b)
+                  for b in budgets] for acc in ("fp32", "weight")}
+    torch.cuda.synchronize()
+    w = outs["weight"]
+    for o in w[1:]:
+        assert torch.equal(o[2], w[0][2]) and torch.equal(o[1], w[0][1])
+        assert float(o[0]) == float(w[0][0])
+    assert _grad_ok(w[0][2], emu["grad_weight"], dtype)
+    d_emu = float((w[0][2].double().cpu() - emu["grad_weight"]).norm())
+    d_exact = float((w[0][2].double().cpu() - exact["grad_weight"]).norm())
+    assert d_emu < d_exact
+    for o in outs["fp32"]:
+        assert _grad_ok(o[2], exact["grad_weight"], dtype)
+        assert torch.equal(o[1], w[0][1])
+        assert float(o[0]) == pytest.approx(exact["loss"], rel=TOL[dtype][0])
+
+
+@pytest.mark.parametrize("accum", ("fp32", "weight"))
+def test_grad_weight_short_k_small_tile_tail(accum):
+    """D = 768, V = 50257, chunks of 512 with a budget of one chunk: every
+    grad_weight product has K = 512, too short to split its last wave of rows
+    along K, so those rows go to a second launch on small tiles (fp32 mode:
+    store, read-modify-write, the last rounding to bf16; 'weight' mode: the
+    running bf16 gradient loaded by each later product)."""
+    BT, D, V, C = 1024, 768, 50257, 512
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=20, seed=59)
+    per_chunk = 50432 * 512 * 2
+    loss, gx, gw, n, bad = F.linear_ce(X.to(DEV), W.to(DEV), t.to(DEV), -100, "mean", 1e-4, C,
+                                       accum, group_bytes=per_chunk)
+    torch.cuda.synchronize()
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, accum, chunk_size=C,
+                                      block_rows=512)
+    assert int(n) == BT - 20 and int(bad) == 0
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
