@@ -218,6 +218,16 @@ __device__ __forceinline__ void zero_row(const CeParams& p, int64_t row) {
   for (int ci = threadIdx.x; ci < r.nch; ci += THREADS) store_chunk<T>(r, ci, static_cast<int>(p.V), z);
 }
 
+// Barrier over LDS reads and writes of the threads only: this wave's LDS
+// instructions complete (lgkmcnt), then all waves meet. Vector memory
+// operations in flight (the next row's loads, direct-to-LDS copies into this
+// thread's own slots, the gradient's stores) stay in flight; __syncthreads, or
+// a release fence on LDS, would wait for them (the copies write LDS). The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Block-wide combine of per-thread (max, sum) pairs; every thread gets the result.
 template <int THREADS>
 __device__ __forceinline__ void block_lse(float& m, float& s, float* sm, float* ss) {
@@ -225,7 +235,7 @@ __device__ __forceinline__ void block_lse(float& m, float& s, float* sm, float* 
   wave_lse_combine(m, s);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { sm[w] = m; ss[w] = s; }
-  __syncthreads();
+  lds_barrier();
   m = sm[0];
   s = ss[0];
 #pragma unroll
@@ -275,17 +285,51 @@ __device__ __forceinline__ int launder_int(int v) {
   return v;
 }
 
+// Target of a row, read through the constant address space: a scalar load
+// (the targets are never written while a kernel runs: the entry points reject
+// a gradient that overlaps them). A vector load would be waited for with the
+// row's chunk loads in flight, and vector memory operations complete in order,
+// so that wait would cover all of them.
+__device__ __forceinline__ int64_t row_target(const CeParams& p, int64_t row) {
+  typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
+  return ((const_i64_ptr)p.target)[row];
+}
+
 // First valid row at or after `row` in steps of `stride`; the ignored rows
 // passed over get a zero loss term and (with a gradient) a zero gradient row.
 template <typename T, int THREADS>
 __device__ __forceinline__ int64_t next_valid_row(const CeParams& p, int64_t row, int64_t stride,
                                                   bool want_grad) {
   for (; row < p.B; row += stride) {
-    if (row_is_valid(p.target[row], p)) break;
+    if (row_is_valid(row_target(p, row), p)) break;
     if (threadIdx.x == 0) p.row_loss[row] = 0.f;
     if (want_grad) zero_row<T, THREADS>(p, row);
   }
   return row;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(N) alone: at most N of this wave's vector memory operations
+// still in flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Chunks [0, PRE) of each thread of row r copied straight into LDS (no
+// registers): chunk k of thread tid lands at lds + (k THREADS + tid) 16, the
+// slot that thread reads back, so no other thread depends on it.
+template <int PRE, int THREADS>
+__device__ __forceinline__ void prefetch_to_lds(char* lds, const RowView& r, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r.in, (lds_ptr_t)(lds + k * THREADS * 16 + wave * 1024), 16, (tid + k * THREADS) * 16, 0,
+        0, kStreamAux);
+  }
 }
 
 // Register-resident rows: THREADS x CPT chunks of 16 B must cover a row.
@@ -295,13 +339,20 @@ __device__ __forceinline__ int64_t next_valid_row(const CeParams& p, int64_t row
 // empty buffer resource: they return zeros and touch no memory.)
 // GRAD: a gradient is written (p.grad != nullptr); a separate instantiation
 // for the loss-only case keeps each variant's registers to its own sweeps.
-// BURST: how the gradient is stored (see sweep 2).
-template <typename T, int THREADS, int CPT, bool GRAD, bool BURST = (THREADS >= 1024)>
+// BURST: how the gradient is stored (see sweep 2). PRE > 0 (with GRAD): the
+// first PRE chunks of every thread's share of the next row are copied into
+// LDS as soon as the current row's sweep has read its own, so that part of
+// the next row streams in while this row's gradient is computed and stored;
+// the other CPT - PRE chunks are loaded into registers after the stores.
+template <typename T, int THREADS, int CPT, bool GRAD, bool BURST = (THREADS >= 1024),
+          int PRE = 0>
 __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
   constexpr int EPC = Elem<T>::kPerChunk;
   constexpr int W = THREADS / 64;
+  static_assert(PRE == 0 || (GRAD && BURST && PRE < CPT), "LDS prefetch with burst stores only");
   __shared__ float sm[2][W], ss[2][W];
   __shared__ float sxt[2];
+  __shared__ __align__(16) char pre_lds[PRE > 0 ? PRE * THREADS * 16 : 16];
   const int tid = threadIdx.x;
   const float scale = reduction_scale(p);
   const uintptr_t base = reinterpret_cast<uintptr_t>(p.logits);
@@ -311,16 +362,22 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
   const int64_t stride = gridDim.x;
   int par = 0;        // LDS slot parity; flips once per valid row (each has one barrier)
   int64_t row = next_valid_row<T, THREADS>(p, blockIdx.x, stride, want_grad);
-  if (row >= p.B) return;
   u32x4 d[CPT];
-  {
+  if (row < p.B) {
     const RowView r0 = row_view<T>(base, gbase, row, p.V, p.ld);
     const int lt = launder_int(tid);
+    if constexpr (PRE > 0) prefetch_to_lds<PRE, THREADS>(pre_lds, r0, lt);
+    // chunks loaded in the order the sweep consumes them (here and at the end
+    // of each row), so that the wait for chunk k leaves the later ones in flight
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) d[k] = load_chunk(r0, lt + k * THREADS);
+    for (int k = PRE; k < CPT; ++k) {
+      d[k] = load_chunk(r0, lt + k * THREADS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  bool first = true;
   while (row < p.B) {
-    const int64_t t = p.target[row];
+    const int64_t t = row_target(p, row);
     const RowView r = row_view<T>(base, gbase, row, p.V, p.ld);
     // the chunk and element that hold x[t]
     const int tpos = r.lead + static_cast<int>(t);
@@ -342,6 +399,16 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
     // Without a gradient the chunk's registers are refilled with the next row
     // at once.
     float m = -kInf, s = 0.f;
+    if constexpr (PRE > 0) {
+      // this row's LDS chunks have landed: after them this wave issued its
+      // register loads (CPT - PRE), and, except for the first row, the
+      // previous row's stores (at least CPT whole-chunk stores)
+      if (first) wait_vm<CPT - PRE>(); else wait_vm<2 * CPT - PRE>();
+      first = false;
+#pragma unroll
+      for (int k = 0; k < PRE; ++k)
+        d[k] = *reinterpret_cast<const u32x4*>(pre_lds + (k * THREADS + tid) * 16);
+    }
     {
       const int lp = launder_int(tid);
 #pragma unroll
@@ -372,6 +439,11 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
+    if constexpr (PRE > 0) {
+      // the sweep has consumed this thread's LDS chunks: refill its slots
+      // with the next row's
+      if (nrow < p.B) prefetch_to_lds<PRE, THREADS>(pre_lds, rn, launder_int(tid));
     }
     block_lse<THREADS>(m, s, sm[par], ss[par]);
     const float log2s = log2_fast(s);          // lse = m + ln(s), m the row max
@@ -442,10 +514,14 @@ __global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
     {
       const int ln = launder_int(tid);
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) d[k] = load_chunk(rn, ln + k * THREADS);
+      for (int k = PRE; k < CPT; ++k) {
+        d[k] = load_chunk(rn, ln + k * THREADS);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     row = nrow;
   }
+  if constexpr (PRE > 0) wait_vm<0>();   // no LDS copy outlives the workgroup
 }
 
 // Rows of any width: two read sweeps with an online max / sum per thread.
@@ -632,7 +708,8 @@ const RowKernel* row_kernels(int* count) {
       {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13, G>), 512, 6656},
       {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 16, G>), 512, 8192},
       {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 12, G>), 1024, 12288},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 16, G>), 1024, 16384},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 16, G, true, G ? 9 : 0>),
+       1024, 16384},
       {reinterpret_cast<const void*>(&ce_rows_stream_kernel<T, 1024>), 1024, 0},
   };
   *count = static_cast<int>(sizeof(k) / sizeof(k[0]));
@@ -649,6 +726,8 @@ int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int64_t ld, int elem_bytes)
   return (epc - 1 + V + epc - 1) / epc;
 }
 
+// Workgroups of a row-kernel launch: as many as are resident on the chip, at
+// most one per row (each walks rows blockIdx, blockIdx + grid, ...).
 static int occupancy_grid(const void* fn, int threads, int64_t rows) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

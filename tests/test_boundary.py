@@ -87,9 +87,9 @@ def test_workspace_sizes():
 
 def test_grad_weight_group_budget_bounds_the_workspace():
     # inputs [BT, 4096] x weight [128256, 4096], chunks of 2048: G^T of one
-    # chunk is 128512 x 2048 bf16 (526 MB)
+    # chunk is 128256 x 2048 bf16 (525 MB; 128256 is a multiple of 256)
     D, V, C = 4096, 128256, 2048
-    gt_chunk = 128512 * 2048 * 2
+    gt_chunk = 128256 * 2048 * 2
     acc32 = V * D * 4
 
     def ws(BT, accum, budget):
