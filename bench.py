@@ -342,20 +342,32 @@ def main() -> int:
             line["value"], line["unit"] = lin["value"], "TFLOP/s"
     line["config"]["workload"] = " + ".join(workload_names)
 
-    # ------------------------------------------------------------ copy ceiling (context)
+    # ------------------------------------------------------------ HBM ceilings (context)
+    # streaming patterns of known size over the CE leg's 4.2 GB buffers: read
+    # only, write only, two copy shapes and the two row patterns of the widest
+    # CE row kernel (in place, rows of the CE workload's width); bytes moved
+    # count a read and a write separately
     if "ce" in legs:
         nb = ce_w.B * ce_w.V * 2
         src, dst = copies[0], copies[1]
-        _lib.lmx_copy(src.data_ptr(), dst.data_ptr(), nb, stream.cuda_stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(3):
-            _lib.lmx_copy(src.data_ptr(), dst.data_ptr(), nb, stream.cuda_stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1) / 3
-        line["copy_ceiling"] = {"value": round(2 * nb / (cms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                                "bytes_moved": 2 * nb}
+        sink = torch.empty(16384, dtype=torch.uint8, device=dev)
+        row_bytes = ce_w.V * 2
+        probes = (("read", _lib.LMX_PROBE_READ, src, sink, nb),
+                  ("write", _lib.LMX_PROBE_WRITE, src, dst, nb),
+                  ("copy", _lib.LMX_PROBE_COPY, src, dst, 2 * nb),
+                  ("copy_batched", _lib.LMX_PROBE_COPY_BATCHED, src, dst, 2 * nb),
+                  ("copy_batched_in_place", _lib.LMX_PROBE_COPY_BATCHED, dst, dst, 2 * nb),
+                  ("rows_interleaved_in_place", _lib.LMX_PROBE_ROWS_INTERLEAVED, dst, dst, 2 * nb),
+                  ("rows_phased_in_place", _lib.LMX_PROBE_ROWS_PHASED, dst, dst, 2 * nb))
+        ceil = {"unit": "GB/s", "buffer_bytes": nb, "row_bytes": row_bytes}
+        for name, mode, a, b, moved in probes:
+            def probe_call(a=a, b=b, mode=mode):
+                _lib.check("lmx_stream_probe", _lib.lmx_stream_probe(
+                    a.data_ptr(), b.data_ptr(), nb, row_bytes, mode, stream.cuda_stream))
+            ms, med = mean_median(per_call_ms(probe_call, 5, 1, stream))
+            ceil[name] = round(moved / (med * 1e-3) / 1e9, 1)
+        log(f"hbm ceilings (GB/s): {ceil}")
+        line["hbm_ceiling"] = ceil
 
     # ------------------------------------------------------------ per-row entry points
     # forward-only reduced CE, selective_log_softmax, the unreduced per-row CE and

@@ -381,6 +381,41 @@ LMX_API const char* lmx_status_string(int status);
  */
 LMX_API int lmx_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/*
+ * lmx_stream_probe -- streaming patterns of known size: the practical HBM
+ * ceilings that the cross-entropy row kernels (one read of the logits, one
+ * write of the gradient) are measured against. A measurement aid like
+ * lmx_copy, not part of either operation. Non-temporal 16-byte accesses.
+ *
+ *   LMX_PROBE_READ             read `bytes` of src (dst: a 16 KiB sink, left
+ *                              untouched in practice)
+ *   LMX_PROBE_WRITE            write `bytes` of dst (src unused, may be NULL)
+ *   LMX_PROBE_COPY             copy src -> dst, 256 threads x 4 chunks per step
+ *   LMX_PROBE_COPY_BATCHED     copy, 1024 threads x 8 chunks (128 KiB) loaded
+ *                              then stored per step, 4 workgroups per CU
+ *   LMX_PROBE_ROWS_INTERLEAVED rows of row_bytes, one 1024-thread workgroup
+ *                              per row, 16 chunks a thread in registers:
+ *                              chunk k of a row stored, then chunk k of the
+ *                              workgroup's next row loaded, in turn
+ *   LMX_PROBE_ROWS_PHASED      the same rows: a row stored whole, then the next
+ *                              row loaded whole
+ *
+ * src and dst 16-byte aligned; bytes a multiple of 16 (LMX_ERR_SIZE); the row
+ * modes need 16 <= row_bytes <= 262144, a multiple of 16 dividing bytes. Copy
+ * and row modes may run in place (dst == src); any other overlap is
+ * LMX_ERR_ALIAS. An unknown mode is LMX_ERR_ENUM.
+ */
+enum {
+  LMX_PROBE_READ = 0,
+  LMX_PROBE_WRITE = 1,
+  LMX_PROBE_COPY = 2,
+  LMX_PROBE_COPY_BATCHED = 3,
+  LMX_PROBE_ROWS_INTERLEAVED = 4,
+  LMX_PROBE_ROWS_PHASED = 5
+};
+LMX_API int lmx_stream_probe(const void* src, void* dst, size_t bytes, size_t row_bytes,
+                             int mode, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

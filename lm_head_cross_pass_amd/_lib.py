@@ -44,6 +44,7 @@ _SIGNATURES = {
     "linear_ce_chunk_rows": (_i64, [_i64, _i64, _i64]),
     "lmx_status_string": (ctypes.c_char_p, [_i32]),
     "lmx_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "lmx_stream_probe": (_i32, [_vp, _vp, _sz, _sz, _i32, _vp]),
     "lmx_scale": (_i32, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "selective_log_softmax": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "ce_loss_rows": (_i32, [_vp, _vp, _i64, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -135,6 +136,15 @@ def linear_ce_chunk_rows(BT, V, chunk_size) -> int:
 
 def lmx_copy(src, dst, nbytes, stream) -> int:
     return load().lmx_copy(src, dst, nbytes, stream)
+
+
+# lmx_stream_probe modes
+(LMX_PROBE_READ, LMX_PROBE_WRITE, LMX_PROBE_COPY, LMX_PROBE_COPY_BATCHED,
+ LMX_PROBE_ROWS_INTERLEAVED, LMX_PROBE_ROWS_PHASED) = range(6)
+
+
+def lmx_stream_probe(src, dst, nbytes, row_bytes, mode, stream) -> int:
+    return load().lmx_stream_probe(src, dst, nbytes, row_bytes, mode, stream)
 
 
 def lmx_scale(src, dst, n, dtype, scale, stream) -> int:

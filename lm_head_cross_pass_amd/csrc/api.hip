@@ -408,4 +408,26 @@ int lmx_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return lmx::copy_enqueue(src, dst, bytes, static_cast<hipStream_t>(stream));
 }
 
+int lmx_stream_probe(const void* src, void* dst, size_t bytes, size_t row_bytes, int mode,
+                     void* stream) {
+  if (mode < LMX_PROBE_READ || mode > LMX_PROBE_ROWS_PHASED) return LMX_ERR_ENUM;
+  if (bytes == 0) return LMX_OK;
+  if (dst == nullptr || (mode != LMX_PROBE_WRITE && src == nullptr)) return LMX_ERR_NULL;
+  if (bytes % 16 != 0) return LMX_ERR_SIZE;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return LMX_ERR_ALIGN;
+  const bool rows = mode == LMX_PROBE_ROWS_INTERLEAVED || mode == LMX_PROBE_ROWS_PHASED;
+  if (rows && (row_bytes == 0 || row_bytes % 16 != 0 || row_bytes > 262144 ||
+               bytes % row_bytes != 0))
+    return LMX_ERR_SIZE;
+  // copies and rows: in place, or two separate buffers; read: dst is a 16 KiB sink
+  if (mode == LMX_PROBE_READ) {
+    if (overlaps(src, bytes, dst, 16384)) return LMX_ERR_ALIAS;
+  } else if (mode != LMX_PROBE_WRITE && src != dst && overlaps(src, bytes, dst, bytes)) {
+    return LMX_ERR_ALIAS;
+  }
+  return lmx::stream_probe_enqueue(src, dst, bytes, row_bytes, mode,
+                                   static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

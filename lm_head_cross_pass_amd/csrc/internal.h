@@ -121,6 +121,8 @@ struct LinearLossChunk {
 int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws, hipStream_t stream);
 
 int copy_enqueue(const void* src, void* dst, size_t bytes, hipStream_t stream);
+int stream_probe_enqueue(const void* src, void* dst, size_t bytes, size_t row_bytes, int mode,
+                         hipStream_t stream);
 
 // dst[i] = RNE(src[i] * (*scale)) in fp32 arithmetic, for n elements of dtype.
 int scale_enqueue(const void* src, void* dst, int64_t n, int dtype, const float* scale,

@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported():
     names = _lib.header_functions()
     assert set(names) == {"ce_fwd_bwd", "ce_workspace_bytes", "ce_fwd_bwd_noalloc", "linear_ce",
                           "linear_ce_workspace_bytes", "linear_ce_chunk_rows",
-                          "lmx_status_string", "lmx_copy", "lmx_scale",
+                          "lmx_status_string", "lmx_copy", "lmx_stream_probe", "lmx_scale",
                           "selective_log_softmax",
                           "ce_loss_rows", "ce_loss_rows_vjp", "linear_loss_logits",
                           "linear_loss_grads", "linear_loss_workspace_bytes"}
@@ -211,6 +211,16 @@ def test_copy_argument_errors():
     assert _lib.lmx_copy(A + 8, A + (1 << 34), 16, None) == _lib.LMX_ERR_ALIGN
     assert _lib.lmx_copy(A, A + 16, 64, None) == _lib.LMX_ERR_ALIAS
     assert _lib.lmx_copy(A, A, 0, None) == _lib.LMX_OK
+    probe = _lib.lmx_stream_probe
+    assert probe(A, A + (1 << 34), 1 << 20, 0, 9, None) == _lib.LMX_ERR_ENUM
+    assert probe(None, A, 1 << 20, 0, _lib.LMX_PROBE_COPY, None) == _lib.LMX_ERR_NULL
+    assert probe(A, A + (1 << 34), (1 << 20) + 8, 0, _lib.LMX_PROBE_COPY, None) == _lib.LMX_ERR_SIZE
+    assert probe(A + 8, A + (1 << 34), 1 << 20, 0, _lib.LMX_PROBE_COPY, None) == _lib.LMX_ERR_ALIGN
+    assert probe(A, A + 64, 1 << 20, 0, _lib.LMX_PROBE_COPY, None) == _lib.LMX_ERR_ALIAS
+    assert probe(A, A + 64, 1 << 20, 0, _lib.LMX_PROBE_READ, None) == _lib.LMX_ERR_ALIAS
+    assert probe(A, A, 1 << 20, 1000, _lib.LMX_PROBE_ROWS_PHASED, None) == _lib.LMX_ERR_SIZE
+    assert probe(A, A, 1 << 20, 1 << 19, _lib.LMX_PROBE_ROWS_PHASED, None) == _lib.LMX_ERR_SIZE
+    assert probe(A, A, 0, 0, _lib.LMX_PROBE_COPY, None) == _lib.LMX_OK
 
 
 def _rows(fn, **kw):
