@@ -53,15 +53,21 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 }
 
 // 16-bit element formats of the linear path, as tags for templates.
+// pack2 narrows two values into one word (low half first); lo / hi widen the
+// halves of such a word.
 struct Bf16 {
   __device__ static float widen(uint16_t h) { return bf16_bits_to_f32(h); }
   __device__ static uint16_t narrow(float x) { return f32_to_bf16_bits(x); }
   __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ static float hi(uint32_t w) { return bf16_hi(w); }
 };
 struct F16 {
   __device__ static float widen(uint16_t h) { return f16_bits_to_f32(h); }
   __device__ static uint16_t narrow(float x) { return f32_to_f16_bits(x); }
   __device__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+  __device__ static float lo(uint32_t w) { return f16_lo(w); }
+  __device__ static float hi(uint32_t w) { return f16_hi(w); }
 };
 
 // v_exp_f32 / v_log_f32 work in base 2.

@@ -34,7 +34,7 @@
 //
 // The epilogue is a functor (see linear_ce.hip): init() sets the accumulators
 // before the K loop, run() stores them after it, and an epilogue with kRounds
-// also rounds them every round_every K steps (round()).
+// also rounds them every round_every K steps (round_tile() on each MFMA tile).
 #pragma once
 
 #include "common.h"
@@ -97,7 +97,7 @@ struct GemmShape {
   int64_t ld_bt;
   int bt_cols;
   // K steps between two roundings of the accumulators by the epilogue (its
-  // round(); only epilogues with kRounds), 0 for none: the weight-dtype
+  // round_tile(); only epilogues with kRounds), 0 for none: the weight-dtype
   // accumulation of grad_weight, one rounding per chunk of the K range.
   int round_every;
 };
@@ -454,7 +454,12 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     if constexpr (Epi::kRounds) {
       // a chunk boundary inside the K range: the epilogue rounds the running
       // sums (the last boundary is the epilogue's own rounding)
-      if (g.round_every > 0 && (ks + 1) % g.round_every == 0 && ks + 1 < ke) epi.round(acc);
+      if (g.round_every > 0 && (ks + 1) % g.round_every == 0 && ks + 1 < ke) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
+      }
     }
     if (g.at_out != nullptr && ks % g.tiles_n == tn) {
       gemm_store_tile_transposed<C, BM>(smem + cur_bytes, g.at_out, g.ld_at, m0, g.at_cols,

@@ -97,8 +97,6 @@ struct EpiOut {
   __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord&, int, int, const GemmShape&) {
     acc_zero(acc);
   }
-  template <int FM, int FN>
-  __device__ void round(f32x16_t (&)[FM][FN]) {}
 
   // Staged path: the tile in LDS as [BM][BN] 16-bit values, the 16-byte pieces
   // of a row XOR-swizzled by bit 2 of (row >> 2), which sends the two halves of
@@ -198,8 +196,6 @@ struct EpiDw {
   __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord&, int, int, const GemmShape&) {
     acc_zero(acc);
   }
-  template <int FM, int FN>
-  __device__ void round(f32x16_t (&)[FM][FN]) {}
 
   template <int MODE, int FM, int FN>
   __device__ void apply(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int n0, const GemmShape& g,
@@ -282,6 +278,9 @@ struct EpiDwW16 {
   int64_t ld;
   const int64_t* mean_count;   // non-null: the mean's N
   int preload;                 // start from the gradient in out16 (a later group)
+  // the mean's 1 / N and N for round_tile(), read once by init(): a load inside
+  // the K loop would wait for every copy in flight
+  float rs = 1.f, rn = 1.f;
 
   EpiDwW16 shifted(int64_t rows, int64_t cols) const {
     EpiDwW16 e = *this;
@@ -298,11 +297,13 @@ struct EpiDwW16 {
   template <int BM, int BN, int FM, int FN>
   __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0,
                        const GemmShape& g) {
+    rs = count_scale(mean_count);
+    rn = count_f(mean_count);
     if (!preload) {
       acc_zero(acc);
       return;
     }
-    const float nf = count_f(mean_count);
+    const float nf = rn;
     const __amdgpu_buffer_rsrc_t r16 = rows_rsrc(out16, m0, g.M - m0, BM, ld * 2);
     const int ldi = static_cast<int>(ld);
     // every load is issued before any value is used (the raw 16 bits go into
@@ -334,15 +335,17 @@ struct EpiDwW16 {
     }
   }
 
-  template <int FM, int FN>
-  __device__ void round(f32x16_t (&acc)[FM][FN]) {
-    const float s = count_scale(mean_count), nf = count_f(mean_count);
+  // a = N * E(a / N) for one MFMA tile's accumulators, two values per
+  // conversion (the empty asm keeps the compiler from splitting the pair
+  // conversion into two single ones)
+  __device__ void round_tile(f32x16_t& a) const {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = E::widen(E::narrow(s * acc[i][j][r])) * nf;
+    for (int r = 0; r < 16; r += 2) {
+      uint32_t w = E::pack2(rs * a[r], rs * a[r + 1]);
+      asm volatile("" : "+v"(w));
+      a[r] = E::lo(w) * rn;
+      a[r + 1] = E::hi(w) * rn;
+    }
   }
 
   template <int BM, int BN, int FM, int FN>
