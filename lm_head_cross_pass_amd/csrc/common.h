@@ -53,12 +53,18 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 }
 
 // 16-bit element formats of the linear path, as tags for templates.
-// pack2 narrows two values into one word (low half first); lo / hi widen the
-// halves of such a word.
+// pack2 narrows two values into one word (low half first); scaled_pack2(s,
+// lo, hi) packs narrow(s * lo) and narrow(s * hi), each exactly as narrow(s * x)
+// rounds (fp16: one rounding of the product, the compiler's mixed-precision
+// fma; bf16: the fp32 product, then the pair conversion); lo / hi widen the
+// halves of a word.
 struct Bf16 {
   __device__ static float widen(uint16_t h) { return bf16_bits_to_f32(h); }
   __device__ static uint16_t narrow(float x) { return f32_to_bf16_bits(x); }
   __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static uint32_t scaled_pack2(float s, float lo, float hi) {
+    return pack_bf16x2(s * lo, s * hi);
+  }
   __device__ static float lo(uint32_t w) { return bf16_lo(w); }
   __device__ static float hi(uint32_t w) { return bf16_hi(w); }
 };
@@ -66,6 +72,9 @@ struct F16 {
   __device__ static float widen(uint16_t h) { return f16_bits_to_f32(h); }
   __device__ static uint16_t narrow(float x) { return f32_to_f16_bits(x); }
   __device__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+  __device__ static uint32_t scaled_pack2(float s, float lo, float hi) {
+    return static_cast<uint32_t>(narrow(s * lo)) | (static_cast<uint32_t>(narrow(s * hi)) << 16);
+  }
   __device__ static float lo(uint32_t w) { return f16_lo(w); }
   __device__ static float hi(uint32_t w) { return f16_hi(w); }
 };

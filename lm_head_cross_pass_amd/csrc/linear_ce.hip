@@ -335,13 +335,13 @@ struct EpiDwW16 {
     }
   }
 
-  // a = N * E(a / N) for one MFMA tile's accumulators, two values per
-  // conversion (the empty asm keeps the compiler from splitting the pair
-  // conversion into two single ones)
+  // a = N * E(a / N) for one MFMA tile's accumulators, rounded exactly as
+  // run() rounds E(s acc), two values per word (the empty asm keeps the
+  // compiler from splitting a pair conversion into two single ones)
   __device__ void round_tile(f32x16_t& a) const {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      uint32_t w = E::pack2(rs * a[r], rs * a[r + 1]);
+      uint32_t w = E::scaled_pack2(rs, a[r], a[r + 1]);
       asm volatile("" : "+v"(w));
       a[r] = E::lo(w) * rn;
       a[r + 1] = E::hi(w) * rn;
