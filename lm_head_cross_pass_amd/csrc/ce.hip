@@ -643,7 +643,10 @@ constexpr int kVjpPerThread = 8;
 constexpr int kVjpChunks = kVjpThreads * kVjpPerThread;
 
 // Raw bits of the element at addr through a scalar (uniform) load of the
-// 4-byte word holding it.
+// 4-byte word holding it. For a 16-bit element that word may include 2 bytes
+// just outside the tensor; like the row kernels' aligned 16-byte chunks, the
+// read stays inside the aligned granule that holds a tensor byte, so it never
+// reaches another page, and the extra half is discarded.
 template <typename T>
 __device__ __forceinline__ uint32_t uniform_elem_bits(uintptr_t addr) {
   typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
