@@ -96,6 +96,34 @@ def test_ce_loss_rows_vjp(B, V, dtype, in_place):
     assert bool((grad.cpu()[target == -100] == 0).all())
 
 
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16, torch.float32))
+@pytest.mark.parametrize("in_place", (False, True))
+def test_vjp_many_rows_per_workgroup(dtype, in_place):
+    """More rows than resident workgroups (each walks several rows, reading the
+    next row's target, g, loss and x[t] while the current one streams), odd V
+    so that rows start at every offset inside a 16-byte chunk, and (in place)
+    a logits base 2 elements past a 16-byte boundary; every row is compared,
+    and the elements around the tensor are left alone."""
+    B, V = 1100, 3001
+    logits, target = workloads.small_ce(B, V, dtype, sigma=2.0, n_ignored=97, seed=77)
+    g = workloads.row_upstream(B, seed=5)
+    loss_in = oracle.cross_entropy_per_row(logits, target, -100).float()
+    off = 2 if in_place else 0
+    buf = torch.full((B * V + 8,), 7.0, dtype=dtype, device=DEV)
+    x = buf[off:off + B * V].view(B, V)
+    x.copy_(logits.to(DEV))
+    assert (x.data_ptr() % 16 != 0) == in_place
+    grad = F.ce_loss_rows_vjp(x, target.to(DEV), loss_in.to(DEV), g.to(DEV), -100,
+                              in_place=in_place)
+    torch.cuda.synchronize()
+    assert (grad.data_ptr() == x.data_ptr()) == in_place
+    ref = oracle.cross_entropy_per_row_vjp(logits, target, g.double(), -100)
+    _vjp_close(grad, ref, g, dtype)
+    assert bool((grad.cpu()[target == -100] == 0).all())
+    outside = torch.cat([buf[:off], buf[off + B * V:]]).cpu()
+    assert bool((outside == 7.0).all())
+
+
 def test_forward_then_vjp_and_autograd():
     B, V = 24, 3001
     logits, target = workloads.small_ce(B, V, torch.float32, sigma=2.0, n_ignored=5, seed=4)
