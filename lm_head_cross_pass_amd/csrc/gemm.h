@@ -83,7 +83,8 @@ struct GemmShape {
   int tiles_m, tiles_n;
   int ksplit;            // number of K splits (1 = none)
   int ksteps_per_split;  // K steps per split
-  // Optional (at_out != nullptr): every A tile also written out transposed,
+  // Optional (at_out != nullptr; only for epilogues with kTransposes): every A
+  // tile also written out transposed,
   // at_out[k * ld_at + m] = A[m][k] for k < K, by one of the tiles_n
   // workgroups that load it (the one whose tile_n is the K step modulo
   // tiles_n); columns m >= at_cols are left alone. Rows of A past M read as
@@ -461,14 +462,16 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
           for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
       }
     }
-    if (g.at_out != nullptr && ks % g.tiles_n == tn) {
-      gemm_store_tile_transposed<C, BM>(smem + cur_bytes, g.at_out, g.ld_at, m0, g.at_cols,
-                                        ks * kGemmBK, g.K);
-    }
-    if (g.bt_out != nullptr && ks % g.tiles_m == tm) {
-      static_assert(C::A_STAGE == C::B_STAGE, "B stages addressed with the A stage offset");
-      gemm_store_tile_transposed<C, BN>(smem + C::B_BASE + cur_bytes, g.bt_out, g.ld_bt, n0,
-                                        g.bt_cols, ks * kGemmBK, g.K);
+    if constexpr (Epi::kTransposes) {
+      if (g.at_out != nullptr && ks % g.tiles_n == tn) {
+        gemm_store_tile_transposed<C, BM>(smem + cur_bytes, g.at_out, g.ld_at, m0, g.at_cols,
+                                          ks * kGemmBK, g.K);
+      }
+      if (g.bt_out != nullptr && ks % g.tiles_m == tm) {
+        static_assert(C::A_STAGE == C::B_STAGE, "B stages addressed with the A stage offset");
+        gemm_store_tile_transposed<C, BN>(smem + C::B_BASE + cur_bytes, g.bt_out, g.ld_bt, n0,
+                                          g.bt_cols, ks * kGemmBK, g.K);
+      }
     }
     if (ks + 1 < ke) {
       // step ks + 1 landed: the copies issued after it (up to AHEAD - 1 steps)

@@ -75,6 +75,7 @@ inline int staged_ok(const void* out, int64_t ld, int64_t n) {
 template <typename E>
 struct EpiOut {
   static constexpr bool kRounds = false;
+  static constexpr bool kTransposes = true;   // may store an operand transposed
   uint16_t* out;
   int64_t ldo;
   float* partial;        // [ksplit][M][ldp]
@@ -178,6 +179,7 @@ enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToW16 = 2, kDwStoreW16 = 
 template <typename E>
 struct EpiDw {
   static constexpr bool kRounds = false;
+  static constexpr bool kTransposes = false;
   float* acc32;     // [V][ld] fp32 accumulator ('fp32' mode)
   uint16_t* out16;  // [V][ld] grad_weight in the weight's format E
   int64_t ld;
@@ -274,6 +276,7 @@ struct EpiDw {
 template <typename E>
 struct EpiDwW16 {
   static constexpr bool kRounds = true;
+  static constexpr bool kTransposes = false;
   uint16_t* out16;  // [V][ld] grad_weight in E
   int64_t ld;
   const int64_t* mean_count;   // non-null: the mean's N
