@@ -72,10 +72,12 @@ inline int staged_ok(const void* out, int64_t ld, int64_t n) {
   return reinterpret_cast<uintptr_t>(out) % 16 == 0 && ld % 8 == 0 && n % 8 == 0 ? 1 : 0;
 }
 
-template <typename E>
+// TR: the product may also store one of its operands transposed (GemmShape's
+// at_out / bt_out); products that never do are compiled without that code.
+template <typename E, bool TR = false>
 struct EpiOut {
   static constexpr bool kRounds = false;
-  static constexpr bool kTransposes = true;   // may store an operand transposed
+  static constexpr bool kTransposes = TR;
   uint16_t* out;
   int64_t ldo;
   float* partial;        // [ksplit][M][ldp]
@@ -473,6 +475,9 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* p, int64_t n) {
 // gemm_interleave_hint); the small tile always uses schedule 0.
 template <int SCHED, typename E, typename Epi>
 int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream) {
+  // an epilogue compiled without the transposed stores must not be given one
+  // to do (no caller does; this keeps a future one from dropping them)
+  if (!Epi::kTransposes && (g.at_out != nullptr || g.bt_out != nullptr)) return LMX_ERR_UNSUPPORTED;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   if (tile == kTileL) {
@@ -630,7 +635,7 @@ int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_
   gs.at_out = gt_out;   // optional: G^T written by the product that reads G
   gs.ld_at = ld_gt;
   gs.at_cols = gt_cols;
-  EpiOut<E> e{gx, ldx, dxp, D, mean_count, staged_ok(gx, ldx, D)};
+  EpiOut<E, true> e{gx, ldx, dxp, D, mean_count, staged_ok(gx, ldx, D)};
   int st = launch_gemm<1, E>(gs, tile, e, stream);
   if (st != LMX_OK) return st;
   if (gs.ksplit > 1) {
@@ -862,10 +867,14 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
         g.bt_out = wt;
         g.ld_bt = ldv;
         g.bt_cols = static_cast<int>(ldv);
+        EpiOut<E, true> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
+        st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
+                            : launch_gemm<1, E>(g, tile, e, stream);
+      } else {
+        EpiOut<E> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
+        st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
+                            : launch_gemm<1, E>(g, tile, e, stream);
       }
-      EpiOut<E> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
-      st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
-                          : launch_gemm<1, E>(g, tile, e, stream);
       if (st != LMX_OK) return st;
     }
     // 3. cross-entropy of the chunk rows, G written over Z, loss terms
