@@ -72,9 +72,15 @@ inline int staged_ok(const void* out, int64_t ld, int64_t n) {
   return reinterpret_cast<uintptr_t>(out) % 16 == 0 && ld % 8 == 0 && n % 8 == 0 ? 1 : 0;
 }
 
+// Output modes of EpiOut fixed at compile time: any (chosen per call from the
+// split and the staged flag), staged 16-bit stores only (an unsplit product
+// with staged set), fp32 split-K partials only (a split product).
+constexpr int kOutAny = 0, kOutStaged = 1, kOutPartial = 2;
+
 // TR: the product may also store one of its operands transposed (GemmShape's
-// at_out / bt_out); products that never do are compiled without that code.
-template <typename E, bool TR = false>
+// at_out / bt_out); products that never do, or whose output mode is fixed,
+// are compiled without the code they do not use.
+template <typename E, bool TR = false, int MODE = kOutAny>
 struct EpiOut {
   static constexpr bool kRounds = false;
   static constexpr bool kTransposes = TR;
@@ -88,6 +94,13 @@ struct EpiOut {
   // the logits product). Needs N, ldo and the output address in multiples of
   // 8 elements / 16 bytes, so that no piece straddles N.
   int staged;
+
+  // Whether a fixed output mode suits the product (host check).
+  bool mode_fits(const GemmShape& g) const {
+    if (MODE == kOutStaged) return g.ksplit == 1 && staged;
+    if (MODE == kOutPartial) return g.ksplit > 1;
+    return true;
+  }
 
   // The same epilogue for the sub-matrix starting at (rows, cols) (direct stores).
   EpiOut shifted(int64_t rows, int64_t cols) const {
@@ -140,11 +153,17 @@ struct EpiOut {
   template <int BM, int BN, int FM, int FN>
   __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int split,
                       const GemmShape& g, uint16_t* smem) {
-    const bool direct = g.ksplit == 1;
     const float s = count_scale(mean_count);
-    if (direct && staged) {
+    if constexpr (MODE == kOutStaged) {
       run_staged<BM, BN, FM, FN>(acc, ac, m0, n0, g, smem, s);
       return;
+    }
+    const bool direct = MODE == kOutPartial ? false : g.ksplit == 1;
+    if constexpr (MODE == kOutAny) {
+      if (direct && staged) {
+        run_staged<BM, BN, FM, FN>(acc, ac, m0, n0, g, smem, s);
+        return;
+      }
     }
     const __amdgpu_buffer_rsrc_t ro =
         direct ? rows_rsrc(out, m0, g.M - m0, BM, ldo * 2)
@@ -182,6 +201,7 @@ template <typename E>
 struct EpiDw {
   static constexpr bool kRounds = false;
   static constexpr bool kTransposes = false;
+  bool mode_fits(const GemmShape&) const { return true; }
   float* acc32;     // [V][ld] fp32 accumulator ('fp32' mode)
   uint16_t* out16;  // [V][ld] grad_weight in the weight's format E
   int64_t ld;
@@ -279,6 +299,7 @@ template <typename E>
 struct EpiDwW16 {
   static constexpr bool kRounds = true;
   static constexpr bool kTransposes = false;
+  bool mode_fits(const GemmShape&) const { return true; }
   uint16_t* out16;  // [V][ld] grad_weight in E
   int64_t ld;
   const int64_t* mean_count;   // non-null: the mean's N
@@ -478,6 +499,7 @@ int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream
   // an epilogue compiled without the transposed stores must not be given one
   // to do (no caller does; this keeps a future one from dropping them)
   if (!Epi::kTransposes && (g.at_out != nullptr || g.bt_out != nullptr)) return LMX_ERR_UNSUPPORTED;
+  if (!epi.mode_fits(g)) return LMX_ERR_UNSUPPORTED;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   if (tile == kTileL) {
@@ -635,8 +657,14 @@ int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_
   gs.at_out = gt_out;   // optional: G^T written by the product that reads G
   gs.ld_at = ld_gt;
   gs.at_cols = gt_cols;
-  EpiOut<E, true> e{gx, ldx, dxp, D, mean_count, staged_ok(gx, ldx, D)};
-  int st = launch_gemm<1, E>(gs, tile, e, stream);
+  int st;
+  if (gs.ksplit > 1) {
+    EpiOut<E, true, kOutPartial> e{gx, ldx, dxp, D, mean_count, 0};
+    st = launch_gemm<1, E>(gs, tile, e, stream);
+  } else {
+    EpiOut<E, true> e{gx, ldx, dxp, D, mean_count, staged_ok(gx, ldx, D)};
+    st = launch_gemm<1, E>(gs, tile, e, stream);
+  }
   if (st != LMX_OK) return st;
   if (gs.ksplit > 1) {
     const int64_t total = static_cast<int64_t>(rows) * D / 4;
@@ -702,7 +730,7 @@ int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int
       const int rows = V - tp.rows0;
       GemmShape b = make_shape(gt + static_cast<int64_t>(tp.rows0) * ldk, ldk, xt, ldk, rows, D,
                                D, K, tp.ksplit, kTileL);
-      EpiOut<E> eo{nullptr, 0, tailp, D, mean_count, 0};   // fp32 partials per split
+      EpiOut<E, false, kOutPartial> eo{nullptr, 0, tailp, D, mean_count, 0};   // fp32 partials per split
       st = launch_gemm<1, E>(b, kTileL, eo, stream);
       if (st != LMX_OK) return st;
       const EpiDw<E> et = e.shifted(tp.rows0, 0);
@@ -870,8 +898,12 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
         EpiOut<E, true> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
         st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
                             : launch_gemm<1, E>(g, tile, e, stream);
+      } else if (staged_ok(z, ldv, ldv)) {
+        EpiOut<E, false, kOutStaged> e{z, ldv, nullptr, 0, nullptr, 1};
+        st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
+                            : launch_gemm<1, E>(g, tile, e, stream);
       } else {
-        EpiOut<E> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
+        EpiOut<E> e{z, ldv, nullptr, 0, nullptr, 0};
         st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
                             : launch_gemm<1, E>(g, tile, e, stream);
       }
