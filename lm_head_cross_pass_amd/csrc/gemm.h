@@ -227,7 +227,7 @@ constexpr int gemm_threads() { return AREA >= 256 * 256 ? 512 : 256; }
 // instruction fills LDS slot (l & 3) of row (l >> 2) of a 16-row block, i.e.
 // it fetches global chunk (l & 3) ^ f(row); per lane only the row / chunk part
 // of the offset is kept, the K step's byte offset goes in the scalar offset.
-template <typename C>
+template <typename C, bool FULLK>
 __device__ __forceinline__ void gemm_copy_stage(char* smem, __amdgpu_buffer_rsrc_t ra,
                                                 __amdgpu_buffer_rsrc_t rb, const int* a_voff,
                                                 const int* b_voff, const int* a_kc,
@@ -235,7 +235,7 @@ __device__ __forceinline__ void gemm_copy_stage(char* smem, __amdgpu_buffer_rsrc
                                                 int K) {
   char* sa = smem + stage * C::A_STAGE + wave * C::A_LOADS * 1024;
   char* sb = smem + C::B_BASE + stage * C::B_STAGE + wave * C::B_LOADS * 1024;
-  if (kbase + kGemmBK <= K) {   // no chunk of this step lies past K
+  if (FULLK || kbase + kGemmBK <= K) {   // no chunk of this step lies past K
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + i * 1024), 16,
@@ -351,7 +351,9 @@ __device__ __forceinline__ void gemm_interleave_hint() {
 }
 
 // E: the operands' 16-bit element format (Bf16 or F16 of common.h).
-template <int BM, int BN, typename Epi, int SCHED, typename E>
+// FULLK: K is a multiple of the K step (no step reaches past K), so the
+// copies need no per-chunk range test.
+template <int BM, int BN, typename Epi, int SCHED, typename E, bool FULLK>
 __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(GemmShape g,
                                                                             Epi epi) {
   using C = GemmCfg<BM, BN>;
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
 #pragma unroll
   for (int s = 0; s < AHEAD; ++s) {
     if (kb + s < ke) {
-      gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
+      gemm_copy_stage<C, FULLK>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
                          __builtin_amdgcn_readfirstlane((kb + s) * kGemmBK), s, wave, g.K);
     }
   }
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     // the stage that step ks - 1 used is free (everyone passed the barrier
     // after reading it): refill it with step ks + AHEAD
     if (ks + AHEAD < ke) {
-      gemm_copy_stage<C>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
+      gemm_copy_stage<C, FULLK>(smem, ra, rb, a_voff, b_voff, a_kc, b_kc,
                          __builtin_amdgcn_readfirstlane((ks + AHEAD) * kGemmBK),
                          __builtin_amdgcn_readfirstlane((t + AHEAD) % kGemmStages), wave, g.K);
     }

@@ -502,14 +502,23 @@ int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream
   if (!epi.mode_fits(g)) return LMX_ERR_UNSUPPORTED;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
+  const bool fullk = g.K % kGemmBK == 0;
   if (tile == kTileL) {
     constexpr int threads = GemmCfg<kTileL, kTileL>::THREADS;
-    hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi, SCHED, E>), dim3(blocks),
-                       dim3(threads), 0, stream, g, epi);
+    if (fullk)
+      hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi, SCHED, E, true>), dim3(blocks),
+                         dim3(threads), 0, stream, g, epi);
+    else
+      hipLaunchKernelGGL((gemm_nt_kernel<kTileL, kTileL, Epi, SCHED, E, false>), dim3(blocks),
+                         dim3(threads), 0, stream, g, epi);
   } else {
     constexpr int threads = GemmCfg<kTileS, kTileS>::THREADS;
-    hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi, 0, E>), dim3(blocks), dim3(threads),
-                       0, stream, g, epi);
+    if (fullk)
+      hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi, 0, E, true>), dim3(blocks),
+                         dim3(threads), 0, stream, g, epi);
+    else
+      hipLaunchKernelGGL((gemm_nt_kernel<kTileS, kTileS, Epi, 0, E, false>), dim3(blocks),
+                         dim3(threads), 0, stream, g, epi);
   }
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
