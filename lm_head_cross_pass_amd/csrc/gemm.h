@@ -101,6 +101,12 @@ struct GemmShape {
   // round_tile(); only epilogues with kRounds), 0 for none: the weight-dtype
   // accumulation of grad_weight, one rounding per chunk of the K range.
   int round_every;
+  // Optional (Bp != nullptr): B given as its fragment-packed copy (layout
+  // below) with bp_ks K steps per 32-row block; the product then runs
+  // gemm_nt_bdir_kernel, which loads B straight into registers. Blocks past
+  // the ones holding rows < b_rows read as zero.
+  const uint16_t* Bp;
+  int bp_ks;
 };
 
 // Block tile BM x BN: 2 x 2 waves for 128 x 128, 2 x 4 waves for 256 x 256;
@@ -483,6 +489,215 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
       gemm_load_frags<C, 0>(smem, a_off, b_off, nxt_bytes, fa0, fb0);
     }
   }
+  epi.template run<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, split, g,
+                                         reinterpret_cast<uint16_t*>(smem));
+}
+
+// ---------------------------------------------------------------- packed B
+//
+// Fragment-packed copy of a K-contiguous operand M [R, K]: 32-row blocks, each
+// a run of K steps of 64, each step four 1 KiB fragments (one per 16-wide k
+// slice) laid out the way the 32 x 32 x 16 MFMA takes its B operand. Element
+// e of lane l of slice q of step s of block b is M[32 b + (l & 31)][64 s +
+// 16 q + 8 (l >> 5) + e] (zero past R or K), stored at
+//   packed[((b * KS + s) * 4 + q) * 512 + 8 l + e].
+// A wave loads each B fragment as one fully coalesced 1 KiB read straight
+// into registers, so B takes no LDS traffic: with B staged in LDS, its
+// direct-to-LDS writes and the fragment reads of both operands are what the
+// K loop waits on; packed, a step moves 160 KiB through LDS instead of 256.
+constexpr int kPackedRows = 32;          // rows per block
+constexpr int kPackedStepBytes = 4096;   // one K step of one block
+
+template <typename C, bool FULLK>
+__device__ __forceinline__ void gemm_copy_a(char* smem, __amdgpu_buffer_rsrc_t ra,
+                                            const int* a_voff, const int* a_kc, int kbase,
+                                            int stage, int wave, int K) {
+  char* sa = smem + stage * C::A_STAGE + wave * C::A_LOADS * 1024;
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ra, (lds_ptr_t)(sa + i * 1024), 16,
+        (FULLK || kbase + a_kc[i] < K) ? a_voff[i] : kOutOfRange, kbase * 2, 0, 0);
+}
+
+// This wave's B fragments of slice KK of the K step at byte offset soff.
+template <typename C, int KK>
+__device__ __forceinline__ void gemm_load_b_slice(u32x4 (&b)[C::FN][4],
+                                                  __amdgpu_buffer_rsrc_t rb, const int* b_voff,
+                                                  int soff) {
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    b[j][KK] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_voff[j] + KK * 1024, soff, 0));
+}
+
+template <typename C, int KK>
+__device__ __forceinline__ void gemm_load_a_frags(const char* smem, const int* a_off,
+                                                  int stage_bytes, u32x4* af) {
+  const int flip = stage_bytes | (KK << 5);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    af[i] = *reinterpret_cast<const u32x4*>(smem + (a_off[i] ^ flip));
+}
+
+template <typename C, typename E, int KK>
+__device__ __forceinline__ void gemm_mfma_slice_b(f32x16_t (&acc)[C::FM][C::FN], const u32x4* af,
+                                                  const u32x4 (&b)[C::FN][4]) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<E>::run(af[i], b[j][KK], acc[i][j]);
+}
+
+// One k slice: MFMA and A fragment read alternate until the FM reads of the
+// next slice are issued, then the remaining MFMAs.
+template <typename C>
+__device__ __forceinline__ void gemm_hint_a_slice() {
+  constexpr int R = C::FM, M = C::FM * C::FN;
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
+}
+
+// C[M, N] = A[M, K] B[N, K]^T with A staged in LDS as in gemm_nt_kernel and
+// B read from its packed copy g.Bp. Each k slice's B fragments are reloaded
+// for the next K step as soon as that slice's MFMAs are issued, so every load
+// has a whole step to land and B needs one set of registers. Every step
+// issues the same copies (past the last step, a copy of the last step into
+// the stage that is free), which keeps the compiler's wait counts exact. The
+// operand formats and the order of the MFMAs over k are those of
+// gemm_nt_kernel, so both kernels give the same bits.
+template <int BM, int BN, typename Epi, typename E, bool FULLK>
+__global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kernel(GemmShape g,
+                                                                                 Epi epi) {
+  using C = GemmCfg<BM, BN>;
+  static_assert(C::THREADS == gemm_threads<BM * BN>(), "thread count");
+  static_assert(kGemmBK == 64 && kGemmStages == 2, "packed steps are 64 wide; two A stages");
+  static_assert((C::A_STAGE & (C::A_STAGE - 1)) == 0, "stage size must be a power of two");
+  static_assert(C::WN % kPackedRows == 0, "a wave's columns are whole packed blocks");
+  __shared__ __align__(16) char smem[C::LDS_BYTES];   // A stages; the epilogue may stage all of it
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+  int split, tm, tn;
+  gemm_tile_of_block(g, split, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int ksteps = (g.K + kGemmBK - 1) / kGemmBK;
+  const int kb = split * g.ksteps_per_split;
+  int ke = kb + g.ksteps_per_split;
+  if (ke > ksteps) ke = ksteps;
+
+  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.M - m0, BM, g.lda * 2);
+  // this wave's FN packed blocks of B (blocks past the existing rows read zero)
+  const int nb0 = __builtin_amdgcn_readfirstlane((n0 + wn * C::WN) / kPackedRows);
+  int nbl = (g.b_rows + kPackedRows - 1) / kPackedRows - nb0;
+  if (nbl > C::FN) nbl = C::FN;
+  if (nbl < 0) nbl = 0;
+  const int nrec = __builtin_amdgcn_readfirstlane(nbl * g.bp_ks * kPackedStepBytes);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(g.Bp) + static_cast<int64_t>(nb0) * g.bp_ks * (kPackedStepBytes / 2),
+      0, nrec, kRawBufFlags);
+
+  const int lrow = lane / C::CPR;
+  const int lslot = lane % C::CPR;
+  int a_voff[C::A_LOADS], a_kc[C::A_LOADS], b_voff[C::FN];
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int r = (wave * C::A_LOADS + i) * C::ROWS_PER_COPY + lrow;
+    a_kc[i] = (lslot ^ lds_swz<C::CPR>(r)) * 8;
+    a_voff[i] = static_cast<int>((static_cast<int64_t>(r) * g.lda + a_kc[i]) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) b_voff[j] = lane * 16 + j * g.bp_ks * kPackedStepBytes;
+
+  const AccCoord ac{wm * C::WM, wn * C::WN, lane};
+  f32x16_t acc[C::FM][C::FN];
+  epi.template init<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, g);
+
+  const int frag_row = lane & 31;
+  const int frag_half = lane >> 5;
+  int a_off[C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int r = wm * C::WM + i * 32 + frag_row;
+    a_off[i] = r * C::ROWB + ((frag_half ^ lds_swz<C::CPR>(r)) << 4);
+  }
+  u32x4 fa0[C::FM], fa1[C::FM];
+  u32x4 bc[C::FN][4];
+  constexpr int BLOADS = C::FN * 4;   // B loads per step
+
+  if (kb < ke) {
+    const int s0 = __builtin_amdgcn_readfirstlane(kb * kPackedStepBytes);
+    gemm_load_b_slice<C, 0>(bc, rb, b_voff, s0);
+    gemm_load_b_slice<C, 1>(bc, rb, b_voff, s0);
+    gemm_load_b_slice<C, 2>(bc, rb, b_voff, s0);
+    gemm_load_b_slice<C, 3>(bc, rb, b_voff, s0);
+    gemm_copy_a<C, FULLK>(smem, ra, a_voff, a_kc, __builtin_amdgcn_readfirstlane(kb * kGemmBK), 0,
+                          wave, g.K);
+    wait_copies<0>();
+    __syncthreads();
+    gemm_load_a_frags<C, 0>(smem, a_off, 0, fa0);
+  }
+  for (int ks = kb; ks < ke; ++ks) {
+    const int t = ks - kb;
+    const int cur = __builtin_amdgcn_readfirstlane((t & 1) * C::A_STAGE);
+    const int nxt = __builtin_amdgcn_readfirstlane(((t + 1) & 1) * C::A_STAGE);
+    // A of step ks + 1 into the stage step ks - 1 used
+    gemm_copy_a<C, FULLK>(smem, ra, a_voff, a_kc,
+                          __builtin_amdgcn_readfirstlane((ks + 1 < ke ? ks + 1 : ks) * kGemmBK),
+                          (t + 1) & 1, wave, g.K);
+    __builtin_amdgcn_sched_barrier(0);
+    // B of step ks + 1, slice by slice as each slice's registers free up (the
+    // last step reloads its own: in bounds and unused)
+    const int sn = __builtin_amdgcn_readfirstlane((ks + 1 < ke ? ks + 1 : ks) * kPackedStepBytes);
+    gemm_load_a_frags<C, 1>(smem, a_off, cur, fa1);
+    gemm_mfma_slice_b<C, E, 0>(acc, fa0, bc);
+    gemm_hint_a_slice<C>();
+    gemm_load_b_slice<C, 0>(bc, rb, b_voff, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_load_a_frags<C, 2>(smem, a_off, cur, fa0);
+    gemm_mfma_slice_b<C, E, 1>(acc, fa1, bc);
+    gemm_hint_a_slice<C>();
+    gemm_load_b_slice<C, 1>(bc, rb, b_voff, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_load_a_frags<C, 3>(smem, a_off, cur, fa1);
+    gemm_mfma_slice_b<C, E, 2>(acc, fa0, bc);
+    gemm_hint_a_slice<C>();
+    gemm_load_b_slice<C, 2>(bc, rb, b_voff, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_mfma_slice_b<C, E, 3>(acc, fa1, bc);
+    gemm_load_b_slice<C, 3>(bc, rb, b_voff, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (Epi::kRounds) {
+      if (g.round_every > 0 && (ks + 1) % g.round_every == 0 && ks + 1 < ke) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
+      }
+    }
+    if constexpr (Epi::kTransposes) {
+      if (g.at_out != nullptr && ks % g.tiles_n == tn) {
+        gemm_store_tile_transposed<C, BM>(smem + cur, g.at_out, g.ld_at, m0, g.at_cols,
+                                          ks * kGemmBK, g.K);
+      }
+    }
+    if (ks + 1 < ke) {
+      // A of step ks + 1 landed (this step's B loads, issued after it, may
+      // still be in flight)
+      wait_copies<BLOADS>();
+      __syncthreads();
+      gemm_load_a_frags<C, 0>(smem, a_off, nxt, fa0);
+    }
+  }
+  // the last step's copy and B loads done, every wave past its last LDS read
+  wait_copies<0>();
+  __syncthreads();
   epi.template run<BM, BN, C::FM, C::FN>(acc, ac, m0, n0, split, g,
                                          reinterpret_cast<uint16_t*>(smem));
 }

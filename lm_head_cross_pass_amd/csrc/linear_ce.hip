@@ -4,11 +4,11 @@
 // page, "chunked_linear_loss" and "chunked_linear_cross_entropy").
 //
 // Per call:   count valid targets (global N, needed before any gradient is
-//             scaled).
+//             scaled); the packed copies (gemm.h) of W and of W^T [D, ldv]
+//             (zero-padded), the B operands of steps 2 and 5.
 // Per chunk of C rows (r0 .. r0 + C'):
-//   1. X_c^T into its columns of X^T [D, ldk]          transpose
-//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM; chunk 0's
-//      also writes W^T [D, ldv] (zero-padded) for step 5 from the W tiles
+//   1. X_c^T into its K steps of the packed X^T [D, ldk]  pack
+//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM
 //   3. the cross-entropy row kernel on Z, in place: loss terms and the
 //      gradient of the summed loss, G = (1 + 2 z lse) softmax - onehot
 //                                                      same kernel as ce_fwd_bwd
@@ -30,9 +30,10 @@
 // epilogue rounds to 16 bits, or all chunks in one product that writes the
 // 16-bit result directly when their G^T fits that budget plus the fp32
 // accumulator's bytes (16384 rows of 4096 at that vocabulary). In
-// 'weight' accumulation the 16-bit grad_weight itself is updated per chunk
-// (rounded to nearest even after each chunk, as the accumulation mode
-// prescribes; ldk = ldc).
+// 'weight' accumulation the gradient is rounded to the 16-bit format after
+// every chunk, as the accumulation mode prescribes: a group's product rounds
+// its running sums at each chunk boundary of its K range, and the next group
+// starts from the 16-bit result.
 //
 // The logits and G are kept in the inputs' 16-bit format (bf16 or fp16)
 // between steps, as the matmuls produce and consume them; the cross-entropy of
@@ -439,6 +440,68 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
+// Packed copy (the fragment-packed B layout of gemm.h) of M [R, K], row
+// stride ld, K a multiple of 8, with KS K steps per 32-row block. Block
+// (b, y) writes steps 4y .. 4y + 3 of row block b; thread t reads 16 bytes
+// (8 k values) of row t / 8 of the block, piece t % 8 of the step.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restrict__ src,
+                                                        int64_t ld, int R, int K,
+                                                        uint16_t* __restrict__ dst, int KS) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int rl = tid >> 3, piece = tid & 7;
+  const int r = b * kPackedRows + rl;
+  // piece p holds k 8p .. 8p + 7 of the step: slice p / 2, lane half p % 2
+  const int lane = rl + 32 * (piece & 1), q = piece >> 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = blockIdx.y * 4 + i;
+    if (s >= KS) break;
+    const int k = s * kGemmBK + 8 * piece;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && k < K) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + k);
+    *reinterpret_cast<u32x4*>(dst + ((static_cast<int64_t>(b) * KS + s) * 4 + q) * 512 + lane * 8) =
+        v;
+  }
+}
+
+// Packed copy of S^T for S [R, Cs] (row stride ld, Cs a multiple of 8): the
+// packed rows are the columns of S and its K runs over the rows of S, zero
+// for rows R .. 64 gridDim.y - 1. Block (c, y) fills K step s_off + y of
+// column block c (KS steps per block) from a 64 x 32 tile of S through LDS.
+__global__ __launch_bounds__(256) void pack_transposed_kernel(const uint16_t* __restrict__ src,
+                                                              int64_t ld, int R, int Cs,
+                                                              uint16_t* __restrict__ dst, int KS,
+                                                              int s_off) {
+  __shared__ uint16_t t[64][kPackedRows + 2];
+  const int cb = blockIdx.x, y = blockIdx.y;
+  const int tid = threadIdx.x;
+  {
+    const int rr = tid >> 2, cc = (tid & 3) * 8;
+    const int r = y * 64 + rr, c = cb * kPackedRows + cc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c < Cs) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[rr][cc + 2 * e] = static_cast<uint16_t>(v[e] & 0xffffu);
+      t[rr][cc + 2 * e + 1] = static_cast<uint16_t>(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    // lane l of slice q: column l & 31, rows 16 q + 8 (l >> 5) .. + 7
+    const int q = tid >> 6, l = tid & 63;
+    const int cl = l & 31, rb = 16 * q + 8 * (l >> 5);
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = static_cast<uint32_t>(t[rb + 2 * e][cl]) |
+             (static_cast<uint32_t>(t[rb + 2 * e + 1][cl]) << 16);
+    *reinterpret_cast<u32x4*>(
+        dst + ((static_cast<int64_t>(cb) * KS + s_off + y) * 4 + q) * 512 + l * 8) = v;
+  }
+}
+
 // grad_inputs rows = E(sum over splits of the fp32 partials), fixed order.
 template <typename E>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
@@ -500,9 +563,31 @@ int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream
   // to do (no caller does; this keeps a future one from dropping them)
   if (!Epi::kTransposes && (g.at_out != nullptr || g.bt_out != nullptr)) return LMX_ERR_UNSUPPORTED;
   if (!epi.mode_fits(g)) return LMX_ERR_UNSUPPORTED;
+  // a packed B never sits in LDS, so it cannot be written out transposed
+  if (g.Bp != nullptr && g.bt_out != nullptr) return LMX_ERR_UNSUPPORTED;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   const bool fullk = g.K % kGemmBK == 0;
+  if (g.Bp != nullptr) {
+    if (tile == kTileL) {
+      constexpr int threads = GemmCfg<kTileL, kTileL>::THREADS;
+      if (fullk)
+        hipLaunchKernelGGL((gemm_nt_bdir_kernel<kTileL, kTileL, Epi, E, true>), dim3(blocks),
+                           dim3(threads), 0, stream, g, epi);
+      else
+        hipLaunchKernelGGL((gemm_nt_bdir_kernel<kTileL, kTileL, Epi, E, false>), dim3(blocks),
+                           dim3(threads), 0, stream, g, epi);
+    } else {
+      constexpr int threads = GemmCfg<kTileS, kTileS>::THREADS;
+      if (fullk)
+        hipLaunchKernelGGL((gemm_nt_bdir_kernel<kTileS, kTileS, Epi, E, true>), dim3(blocks),
+                           dim3(threads), 0, stream, g, epi);
+      else
+        hipLaunchKernelGGL((gemm_nt_bdir_kernel<kTileS, kTileS, Epi, E, false>), dim3(blocks),
+                           dim3(threads), 0, stream, g, epi);
+    }
+    return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
+  }
   if (tile == kTileL) {
     constexpr int threads = GemmCfg<kTileL, kTileL>::THREADS;
     if (fullk)
@@ -545,7 +630,9 @@ int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t strea
     a.N = cols;
     a.b_rows = g.b_rows < cols ? g.b_rows : cols;
     a.tiles_n = n1;
-    b.B = g.B + static_cast<int64_t>(cols) * g.ldb;
+    if (g.B != nullptr) b.B = g.B + static_cast<int64_t>(cols) * g.ldb;
+    if (g.Bp != nullptr)
+      b.Bp = g.Bp + static_cast<int64_t>(cols / kPackedRows) * g.bp_ks * (kPackedStepBytes / 2);
     b.N = g.N - cols;
     b.b_rows = g.b_rows > cols ? g.b_rows - cols : 0;
     b.tiles_m = (g.M + kTileS - 1) / kTileS;
@@ -613,6 +700,8 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.ld_bt = 0;
   g.bt_cols = 0;
   g.round_every = 0;
+  g.Bp = nullptr;
+  g.bp_ks = 0;
   return g;
 }
 
@@ -622,6 +711,34 @@ int transpose_pad(const uint16_t* src, int64_t ld_src, int R, int Cs, uint16_t* 
   dim3 grid(Rp / 64, (Cs + 63) / 64);
   hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, stream, src, ld_src, R, Cs, dst,
                      ld_dst);
+  return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
+}
+
+// Steps and bytes of a packed copy of an operand with `rows` rows and K = k.
+int64_t packed_steps(int64_t k) { return (k + kGemmBK - 1) / kGemmBK; }
+size_t packed_bytes(int64_t rows, int64_t k) {
+  return static_cast<size_t>((rows + kPackedRows - 1) / kPackedRows) * packed_steps(k) *
+         kPackedStepBytes;
+}
+
+// Packed copy of M [R, K] (row stride ld) with KS steps per block.
+int pack_rows(const uint16_t* src, int64_t ld, int R, int K, int KS, uint16_t* dst,
+              hipStream_t stream) {
+  if (R == 0 || KS == 0) return LMX_OK;
+  dim3 grid((R + kPackedRows - 1) / kPackedRows, (KS + 3) / 4);
+  hipLaunchKernelGGL(pack_rows_kernel, grid, dim3(256), 0, stream, src, ld, R, K, dst, KS);
+  return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
+}
+
+// Packed copy of S^T for S [R, Cs] (row stride ld): K steps s_off .. s_off +
+// Rp / 64 - 1 of a packed buffer with KS steps per block (rows R .. Rp - 1 of
+// S read as zero; Rp a multiple of 64).
+int pack_transposed(const uint16_t* src, int64_t ld, int R, int Cs, int Rp, uint16_t* dst, int KS,
+                    int s_off, hipStream_t stream) {
+  if (Rp == 0 || Cs == 0) return LMX_OK;
+  dim3 grid((Cs + kPackedRows - 1) / kPackedRows, Rp / kGemmBK);
+  hipLaunchKernelGGL(pack_transposed_kernel, grid, dim3(256), 0, stream, src, ld, R, Cs, dst, KS,
+                     s_off);
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
@@ -649,20 +766,23 @@ DxPlan dx_plan(int64_t C, int64_t D, int64_t ldv) {
   return {kTileS, static_cast<int>(ss)};
 }
 
-// grad_inputs rows of one chunk: G [rows, lda_g] times W, with W^T [D, ldv] as
-// the K-contiguous operand over K = k_len vocabulary columns, scaled by
+// grad_inputs rows of one chunk: G [rows, lda_g] times W, with W^T [D, ldv] in
+// its packed copy wtp (ldv / 64 K steps a block) as the B operand over K =
+// k_len vocabulary columns, scaled by
 // 1 / *mean_count when that is given; split-K partials in dxp when the layout
 // chose splits. With gt_out, the product also writes G^T (gt_out[v * ld_gt +
 // r] for r < gt_cols, zeros for r >= rows) from the G tiles it loads, in place
 // of a separate transpose; the caller passes it only when the chunk's tiles
 // cover all gt_cols columns (a full chunk).
 template <typename E>
-int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_t* wt,
+int chunk_grad_inputs(const uint16_t* g, int64_t lda_g, int k_len, const uint16_t* wtp,
                       int64_t ldv, int rows, int D, int64_t chunk, int ksplit, float* dxp,
                       uint16_t* gx, int64_t ldx, const int64_t* mean_count, uint16_t* gt_out,
                       int64_t ld_gt, int gt_cols, hipStream_t stream) {
   const int tile = dx_plan(chunk, D, ldv).tile;   // the plan the workspace was sized for
-  GemmShape gs = make_shape(g, lda_g, wt, ldv, rows, D, D, k_len, ksplit, tile);
+  GemmShape gs = make_shape(g, lda_g, nullptr, 0, rows, D, D, k_len, ksplit, tile);
+  gs.Bp = wtp;
+  gs.bp_ks = static_cast<int>(packed_steps(ldv));
   gs.at_out = gt_out;   // optional: G^T written by the product that reads G
   gs.ld_at = ld_gt;
   gs.at_cols = gt_cols;
@@ -716,17 +836,20 @@ size_t dw_tail_bytes(int64_t V, int64_t D, int64_t K) {
   return t.ksplit > 1 ? static_cast<size_t>(t.ksplit) * (V - t.rows0) * D * 4 : 0;
 }
 
-// grad_weight product G^T X over K columns of G^T [V, ldk] and X^T [D, ldk],
-// scaled by 1 / *mean_count when that is given, stored or accumulated
+// grad_weight product G^T X over K columns of G^T [V, ldk] and X^T [D, ldk]
+// (the packed copy xtp, ldk / 64 K steps a block), scaled by 1 / *mean_count
+// when that is given, stored or accumulated
 // according to `mode`. tailp (tail_bytes of workspace) holds the K-split
 // partials of the last rows when dw_tail_plan splits them.
 template <typename E>
-int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int K, int V, int D,
+int grad_weight_product(const uint16_t* gt, const uint16_t* xtp, int64_t ldk, int K, int V, int D,
                         float* dw, uint16_t* gw, int64_t ldw, int mode,
                         const int64_t* mean_count, float* tailp, size_t tail_bytes,
                         hipStream_t stream) {
   const int tile = pick_tile(V, D);
-  GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
+  GemmShape gs = make_shape(gt, ldk, nullptr, 0, V, D, D, K, 1, tile);
+  gs.Bp = xtp;
+  gs.bp_ks = static_cast<int>(packed_steps(ldk));
   EpiDw<E> e{dw, gw, ldw, mode, mean_count};
   if (tile == kTileL && tailp != nullptr && dw_tail_bytes(V, D, K) <= tail_bytes) {
     const DwTail tp = dw_tail_plan(V, D, K);
@@ -737,8 +860,10 @@ int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int
       int st = launch_gemm<1, E>(a, kTileL, e, stream);
       if (st != LMX_OK) return st;
       const int rows = V - tp.rows0;
-      GemmShape b = make_shape(gt + static_cast<int64_t>(tp.rows0) * ldk, ldk, xt, ldk, rows, D,
-                               D, K, tp.ksplit, kTileL);
+      GemmShape b = make_shape(gt + static_cast<int64_t>(tp.rows0) * ldk, ldk, nullptr, 0, rows,
+                               D, D, K, tp.ksplit, kTileL);
+      b.Bp = gs.Bp;
+      b.bp_ks = gs.bp_ks;
       EpiOut<E, false, kOutPartial> eo{nullptr, 0, tailp, D, mean_count, 0};   // fp32 partials per split
       st = launch_gemm<1, E>(b, kTileL, eo, stream);
       if (st != LMX_OK) return st;
@@ -761,11 +886,13 @@ int grad_weight_product(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int
 // needs the chunks in order within one workgroup, so a ragged last wave goes
 // to small tiles instead.
 template <typename E>
-int grad_weight_product_w16(const uint16_t* gt, const uint16_t* xt, int64_t ldk, int K, int V,
+int grad_weight_product_w16(const uint16_t* gt, const uint16_t* xtp, int64_t ldk, int K, int V,
                             int D, uint16_t* gw, int64_t ldw, const int64_t* mean_count,
                             int round_every, bool preload, hipStream_t stream) {
   const int tile = pick_tile(V, D);
-  GemmShape gs = make_shape(gt, ldk, xt, ldk, V, D, D, K, 1, tile);
+  GemmShape gs = make_shape(gt, ldk, nullptr, 0, V, D, D, K, 1, tile);
+  gs.Bp = xtp;
+  gs.bp_ks = static_cast<int>(packed_steps(ldk));
   gs.round_every = round_every;
   EpiDwW16<E> e{gw, ldw, mean_count, preload ? 1 : 0};
   return tile == kTileL ? launch_gemm_split_tail<1, E>(gs, e, stream)
@@ -778,11 +905,11 @@ int grad_weight_product_w16(const uint16_t* gt, const uint16_t* xt, int64_t ldk,
 // dtype's per-chunk rounding.
 template <typename E>
 int grad_weight_group(int accum, int64_t gi, int64_t ngroups, const uint16_t* gt,
-                      const uint16_t* xt, int64_t ldk, int K, int64_t ldc, int V, int D,
+                      const uint16_t* xtp, int64_t ldk, int K, int64_t ldc, int V, int D,
                       float* dw, uint16_t* gw, int64_t ldw, const int64_t* mean_count,
                       float* tailp, size_t tail_bytes, hipStream_t stream) {
   if (accum == LMX_ACC_WEIGHT) {
-    return grad_weight_product_w16<E>(gt, xt, ldk, K, V, D, gw, ldw, mean_count,
+    return grad_weight_product_w16<E>(gt, xtp, ldk, K, V, D, gw, ldw, mean_count,
                                       static_cast<int>(ldc / kGemmBK), gi > 0, stream);
   }
   const bool first = gi == 0, last = gi == ngroups - 1;
@@ -790,7 +917,7 @@ int grad_weight_group(int accum, int64_t gi, int64_t ngroups, const uint16_t* gt
                    : first      ? kDwStoreF32
                    : last       ? kDwAddF32ToW16
                                 : kDwAddF32;
-  return grad_weight_product<E>(gt, xt, ldk, K, V, D, dw, gw, ldw, mode, mean_count, tailp,
+  return grad_weight_product<E>(gt, xtp, ldk, K, V, D, dw, gw, ldw, mode, mean_count, tailp,
                                 tail_bytes, stream);
 }
 
@@ -844,8 +971,11 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.row_loss_off = take(static_cast<size_t>(BT) * 4);
   w.z_off = take(generic ? 0 : static_cast<size_t>(C) * w.ldv * 2);
   w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldk * 2);
-  w.xt_off = take(static_cast<size_t>(D) * w.ldk * 2);
-  w.wt_off = take(static_cast<size_t>(D) * w.ldv * 2);
+  // packed copies (gemm.h) of the products' B operands: X^T [D, ldk], W^T
+  // [D, ldv] and, for the fused path's logits, W [V, D]
+  w.xt_off = take(packed_bytes(D, w.ldk));
+  w.wt_off = take(packed_bytes(D, w.ldv));
+  w.wp_off = take(generic ? 0 : packed_bytes(V, D));
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
   w.dw_off = take(accum == LMX_ACC_F32 && nchunks > w.dw_group ? static_cast<size_t>(V) * D * 4
                                                                  : 0);
@@ -866,14 +996,17 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
   float* row_loss = reinterpret_cast<float*>(ws + wl.row_loss_off);
   uint16_t* z = reinterpret_cast<uint16_t*>(ws + wl.z_off);
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
-  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
+  uint16_t* xtp = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
+  uint16_t* wtp = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
+  uint16_t* wp = reinterpret_cast<uint16_t*>(ws + wl.wp_off);
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
   float* dwp = reinterpret_cast<float*>(ws + wl.dwp_off);
   const int D = static_cast<int>(p.D), V = static_cast<int>(p.V);
   const int64_t ldv = wl.ldv, ldc = wl.ldc, ldk = wl.ldk, grp = wl.dw_group;
   const int64_t* mean_count = p.reduction == LMX_MEAN ? n_ws : nullptr;
+  const int ks_d = static_cast<int>(packed_steps(D)), ks_v = static_cast<int>(packed_steps(ldv));
+  const int ks_k = static_cast<int>(packed_steps(ldk));
 
   int st = count_enqueue(p.target, p.BT, p.V, p.ignore_index, n_ws, p.n_valid_user, p.bad_user,
                          stream);
@@ -884,8 +1017,12 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
     return finish_enqueue(row_loss, 0, n_ws, p.reduction, p.loss, stream);
   }
-  // W^T [D, ldv] for the grad_inputs products is written by chunk 0's logits
-  // product, which loads every tile of W (zero rows past V give the padding)
+  // packed copies of W (the logits products' B) and of W^T [D, ldv] (the
+  // grad_inputs products' B; rows of W past V give zero columns)
+  st = pack_rows(p.w, p.D, V, D, ks_d, wp, stream);
+  if (st != LMX_OK) return st;
+  st = pack_transposed(p.w, p.D, V, D, static_cast<int>(ldv), wtp, ks_v, 0, stream);
+  if (st != LMX_OK) return st;
   const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t r0 = c * p.chunk;
@@ -893,21 +1030,17 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     const uint16_t* xc = p.x + r0 * p.D;
     const int64_t* tc = p.target + r0;
     const int64_t slot = c % grp;   // this chunk's columns in G^T and X^T
-    // 1. X_c^T
-    st = transpose_pad(xc, p.D, rows, D, xt + slot * ldc, ldk, static_cast<int>(ldc), stream);
+    // 1. X_c^T, packed, as this chunk's K steps of the group's X^T
+    st = pack_transposed(xc, p.D, rows, D, static_cast<int>(ldc), xtp, ks_k,
+                         static_cast<int>(slot * ldc / kGemmBK), stream);
     if (st != LMX_OK) return st;
     // 2. logits Z = X_c W^T over all ldv columns (columns >= V read zero rows of W)
     {
       const int tile = pick_tile(rows, ldv);
       GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
-      if (c == 0) {
-        g.bt_out = wt;
-        g.ld_bt = ldv;
-        g.bt_cols = static_cast<int>(ldv);
-        EpiOut<E, true> e{z, ldv, nullptr, 0, nullptr, staged_ok(z, ldv, ldv)};
-        st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
-                            : launch_gemm<1, E>(g, tile, e, stream);
-      } else if (staged_ok(z, ldv, ldv)) {
+      g.Bp = wp;
+      g.bp_ks = ks_d;
+      if (staged_ok(z, ldv, ldv)) {
         EpiOut<E, false, kOutStaged> e{z, ldv, nullptr, 0, nullptr, 1};
         st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
                             : launch_gemm<1, E>(g, tile, e, stream);
@@ -943,14 +1076,14 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
       if (st != LMX_OK) return st;
     }
     // 5. grad_inputs rows
-    st = chunk_grad_inputs<E>(z, ldv, static_cast<int>(ldv), wt, ldv, rows, D, p.chunk,
+    st = chunk_grad_inputs<E>(z, ldv, static_cast<int>(ldv), wtp, ldv, rows, D, p.chunk,
                               static_cast<int>(wl.ksplit), dxp, p.grad_x + r0 * p.D, p.D,
                               mean_count, fuse_gt ? gt + slot * ldc : nullptr, ldk,
                               static_cast<int>(ldc), stream);
     if (st != LMX_OK) return st;
     // 6. grad_weight, once per group of chunks
     if (slot == grp - 1 || c == nchunks - 1) {
-      st = grad_weight_group<E>(p.accum, c / grp, (nchunks + grp - 1) / grp, gt, xt, ldk,
+      st = grad_weight_group<E>(p.accum, c / grp, (nchunks + grp - 1) / grp, gt, xtp, ldk,
                                 static_cast<int>((slot + 1) * ldc), ldc, V, D, dw, p.grad_w, p.D,
                                 mean_count, dwp, wl.dwp_bytes, stream);
       if (st != LMX_OK) return st;
@@ -975,8 +1108,8 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   const LinearCeWorkspace wl = linear_ce_workspace_layout(p.BT, p.D, p.V, p.chunk, p.accum, true, 0);
   char* ws = static_cast<char*>(ws_base);
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
-  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
+  uint16_t* xtp = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
+  uint16_t* wtp = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
   float* dwp = reinterpret_cast<float*>(ws + wl.dwp_off);
@@ -985,11 +1118,14 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
   const int64_t slot = p.index % grp;   // this chunk's columns in G^T and X^T
   int st;
-  if (p.index == 0) {   // W^T for every chunk of the pass
-    st = transpose_pad(p.w, p.D, V, D, wt, ldv, static_cast<int>(ldv), stream);
+  if (p.index == 0) {   // packed W^T for every chunk of the pass
+    st = pack_transposed(p.w, p.D, V, D, static_cast<int>(ldv), wtp,
+                         static_cast<int>(packed_steps(ldv)), 0, stream);
     if (st != LMX_OK) return st;
   }
-  st = transpose_pad(p.xc, p.D, p.rows, D, xt + slot * ldc, ldk, static_cast<int>(ldc), stream);
+  st = pack_transposed(p.xc, p.D, p.rows, D, static_cast<int>(ldc), xtp,
+                       static_cast<int>(packed_steps(ldk)), static_cast<int>(slot * ldc / kGemmBK),
+                       stream);
   if (st != LMX_OK) return st;
   const bool fuse_gt = p.rows == p.chunk;   // G^T from the grad_inputs product
   if (!fuse_gt) {
@@ -997,7 +1133,7 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
                        stream);
     if (st != LMX_OK) return st;
   }
-  st = chunk_grad_inputs<E>(p.g, p.ld_g, V, wt, ldv, p.rows, D, p.chunk,
+  st = chunk_grad_inputs<E>(p.g, p.ld_g, V, wtp, ldv, p.rows, D, p.chunk,
                             static_cast<int>(wl.ksplit), dxp, p.grad_xc, p.D, nullptr,
                             fuse_gt ? gt + slot * ldc : nullptr, ldk, static_cast<int>(ldc),
                             stream);
@@ -1005,7 +1141,7 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   // grad_weight, once per group of chunks (the group's G^T and X^T columns
   // stay in the workspace between the calls)
   if (slot != grp - 1 && p.index != nchunks - 1) return LMX_OK;
-  return grad_weight_group<E>(p.accum, p.index / grp, (nchunks + grp - 1) / grp, gt, xt, ldk,
+  return grad_weight_group<E>(p.accum, p.index / grp, (nchunks + grp - 1) / grp, gt, xtp, ldk,
                               static_cast<int>((slot + 1) * ldc), ldc, V, D, dw, p.grad_w, p.D,
                               nullptr, dwp, wl.dwp_bytes, stream);
 }
