@@ -79,6 +79,7 @@ struct GemmShape {
   const uint16_t* B;
   int64_t ldb;
   int M, N, K;
+  int a_rows;            // rows of A that exist (M may extend past them into zeros)
   int b_rows;            // rows of B that exist (N may extend past them into zeros)
   int tiles_m, tiles_n;
   int ksplit;            // number of K splits (1 = none)
@@ -92,6 +93,10 @@ struct GemmShape {
   uint16_t* at_out;
   int64_t ld_at;
   int at_cols;
+  // at_pk_ks > 0 (gemm_nt_bdir_kernel only): at_out is instead the packed copy
+  // (layout below) of A^T, whose rows are A's K and whose K runs over A's rows,
+  // with at_pk_ks K steps per block; ld_at is then unused.
+  int at_pk_ks;
   // The same for B (bt_out[k * ld_bt + n] = B[n][k], columns n < bt_cols), by
   // the one of the tiles_m workgroups whose tile_m is the K step modulo tiles_m.
   uint16_t* bt_out;
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
   int ke = kb + g.ksteps_per_split;
   if (ke > ksteps) ke = ksteps;
 
-  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.M - m0, BM, g.lda * 2);
+  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.a_rows - m0, BM, g.lda * 2);
   const __amdgpu_buffer_rsrc_t rb = rows_rsrc(g.B, n0, g.b_rows - n0, BN, g.ldb * 2);
 
   const int lrow = lane / C::CPR;
@@ -549,6 +554,47 @@ __device__ __forceinline__ void gemm_mfma_slice_b(f32x16_t (&acc)[C::FM][C::FN],
     for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<E>::run(af[i], b[j][KK], acc[i][j]);
 }
 
+// Writes the A tile of one K step (R rows x 64 k in the LDS stage at `st`,
+// row pieces swizzled as the copies left them) into the packed copy of A^T
+// (rows = k, K = A's rows, ks K steps per block), for tile rows r0 + r <
+// cols and k below K rounded up to a whole block (the k past K read as zero).
+// As in gemm_store_tile_transposed, a thread transposes an 8 x 8 block in
+// registers; piece j of it (k = kbase + 8c + j, rows r0 + 8b .. + 7) is
+// lane (k % 32) + 32 ((r0 + 8b) / 8 % 2) of slice (r0 + 8b) / 16 % 4 of step
+// (r0 + 8b) / 64 of block k / 32, so the 8 pieces fill 128 contiguous bytes.
+template <typename C, int R>
+__device__ __forceinline__ void gemm_store_tile_packed_t(const char* st, uint16_t* out, int ks,
+                                                        int r0, int cols, int kbase, int K) {
+  constexpr int RB = R / 8;
+  constexpr int BLOCKS = RB * (kGemmBK / 8);
+  const int k_end = (K + kPackedRows - 1) / kPackedRows * kPackedRows;
+  for (int t = static_cast<int>(threadIdx.x); t < BLOCKS; t += C::THREADS) {
+    const int b = t % RB, c = t / RB;
+    if (r0 + 8 * b + 8 > cols || kbase + 8 * c >= k_end) continue;
+    u32x4 in[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * b + i;
+      in[i] = *reinterpret_cast<const u32x4*>(st + r * C::ROWB + ((c ^ lds_swz<C::CPR>(r)) << 4));
+    }
+    const int v0 = r0 + 8 * b, k0 = kbase + 8 * c;
+    uint16_t* dst = out + ((static_cast<int64_t>(k0 / kPackedRows) * ks + v0 / kGemmBK) * 4 +
+                           (v0 / 16) % 4) * 512 +
+                    ((k0 % kPackedRows) + 32 * ((v0 / 8) % 2)) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = in[2 * q][j >> 1], hi = in[2 * q + 1][j >> 1];
+        o[q] = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                       : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+      *reinterpret_cast<u32x4*>(dst + j * 8) = o;
+    }
+  }
+}
+
 // One k slice: MFMA and A fragment read alternate until the FM reads of the
 // next slice are issued, then the remaining MFMAs.
 template <typename C>
@@ -592,7 +638,7 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kerne
   int ke = kb + g.ksteps_per_split;
   if (ke > ksteps) ke = ksteps;
 
-  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.M - m0, BM, g.lda * 2);
+  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(g.A, m0, g.a_rows - m0, BM, g.lda * 2);
   // this wave's FN packed blocks of B (blocks past the existing rows read zero)
   const int nb0 = __builtin_amdgcn_readfirstlane((n0 + wn * C::WN) / kPackedRows);
   int nbl = (g.b_rows + kPackedRows - 1) / kPackedRows - nb0;
@@ -683,8 +729,12 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kerne
     }
     if constexpr (Epi::kTransposes) {
       if (g.at_out != nullptr && ks % g.tiles_n == tn) {
-        gemm_store_tile_transposed<C, BM>(smem + cur, g.at_out, g.ld_at, m0, g.at_cols,
+        if (g.at_pk_ks > 0)
+          gemm_store_tile_packed_t<C, BM>(smem + cur, g.at_out, g.at_pk_ks, m0, g.at_cols,
                                           ks * kGemmBK, g.K);
+        else
+          gemm_store_tile_transposed<C, BM>(smem + cur, g.at_out, g.ld_at, m0, g.at_cols,
+                                            ks * kGemmBK, g.K);
       }
     }
     if (ks + 1 < ke) {

@@ -191,6 +191,77 @@ struct EpiOut {
   }
 };
 
+// Step 2 with its operands swapped: the product runs over (vocabulary row m,
+// token n), W as A (through LDS) and the chunk's packed X_c as B, and this
+// epilogue writes the tile transposed, out[n][m] = E(acc), for m < m_out (rows
+// of A past M are zeros: the padding columns) and n < N. Through LDS: the tile
+// staged as [BN][BM] 16-bit values, each lane writing its four consecutive m
+// of a column as one 8-byte unit, the units of row n XOR-swizzled by an even
+// value from n (so the 32 rows a half-wave writes land in distinct banks, and
+// a 16-byte piece of a row stays two adjacent units in order); then whole
+// 16-byte pieces of out's rows stored. TR: chunk 0's product also writes the
+// packed W^T from its A tiles (GemmShape's at_out with at_pk_ks).
+template <typename E, bool TR>
+struct EpiOutT {
+  static constexpr bool kRounds = false;
+  static constexpr bool kTransposes = TR;
+  uint16_t* out;
+  int64_t ldo;
+  int m_out;
+
+  bool mode_fits(const GemmShape& g) const { return g.ksplit == 1; }
+
+  // The same epilogue for the product's sub-matrix starting at (rows, cols).
+  EpiOutT shifted(int64_t rows, int64_t cols) const {
+    EpiOutT e = *this;
+    e.out = out + cols * ldo + rows;
+    e.m_out = m_out - static_cast<int>(rows);
+    return e;
+  }
+
+  template <int BM, int BN, int FM, int FN>
+  __device__ void init(f32x16_t (&acc)[FM][FN], const AccCoord&, int, int, const GemmShape&) {
+    acc_zero(acc);
+  }
+
+  template <int BM, int BN, int FM, int FN>
+  __device__ void run(f32x16_t (&acc)[FM][FN], const AccCoord& ac, int m0, int n0, int,
+                      const GemmShape& g, uint16_t* smem) {
+    static_assert(BM * BN * 2 <= GemmCfg<BM, BN>::LDS_BYTES, "the tile must fit the LDS");
+    constexpr int UNITS = BM / 4;                 // 8-byte units per staged row
+    constexpr int SWM = (UNITS / 2 - 1) << 1;     // even swizzle values below UNITS
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = ac.col(j);
+      const int sw = (n << 1) & SWM;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int u = ac.row(i, 4 * r4) >> 2;   // rows 4 r4 .. 4 r4 + 3 of the lane: one unit
+          uint2 v;
+          v.x = static_cast<uint32_t>(E::narrow(acc[i][j][4 * r4])) |
+                (static_cast<uint32_t>(E::narrow(acc[i][j][4 * r4 + 1])) << 16);
+          v.y = static_cast<uint32_t>(E::narrow(acc[i][j][4 * r4 + 2])) |
+                (static_cast<uint32_t>(E::narrow(acc[i][j][4 * r4 + 3])) << 16);
+          *reinterpret_cast<uint2*>(smem + n * BM + ((u ^ sw) << 2)) = v;
+        }
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t ro = rows_rsrc(out, n0, g.N - n0, BN, ldo * 2);
+    constexpr int PPR = BM / 8;   // 16-byte pieces per staged row
+    for (int idx = static_cast<int>(threadIdx.x); idx < BN * PPR; idx += static_cast<int>(blockDim.x)) {
+      const int n = idx / PPR, piece = idx % PPR;
+      if (m0 + piece * 8 >= m_out) continue;
+      const int sw = (n << 1) & SWM;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + n * BM + (((2 * piece) ^ sw) << 2));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (n * static_cast<int>(ldo) + m0 + piece * 8) * 2,
+                                             0, 0);
+    }
+  }
+};
+
 // grad_weight epilogue modes; "W16" is the weight's 16-bit format (bf16 / fp16).
 // ('weight' accumulation has its own epilogue, EpiDwW16.)
 enum DwMode { kDwStoreF32 = 0, kDwAddF32 = 1, kDwAddF32ToW16 = 2, kDwStoreW16 = 3 };
@@ -563,8 +634,10 @@ int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream
   // to do (no caller does; this keeps a future one from dropping them)
   if (!Epi::kTransposes && (g.at_out != nullptr || g.bt_out != nullptr)) return LMX_ERR_UNSUPPORTED;
   if (!epi.mode_fits(g)) return LMX_ERR_UNSUPPORTED;
-  // a packed B never sits in LDS, so it cannot be written out transposed
+  // a packed B never sits in LDS, so it cannot be written out transposed; a
+  // packed A^T is written by the packed-B kernel only
   if (g.Bp != nullptr && g.bt_out != nullptr) return LMX_ERR_UNSUPPORTED;
+  if (g.Bp == nullptr && g.at_out != nullptr && g.at_pk_ks > 0) return LMX_ERR_UNSUPPORTED;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   const bool fullk = g.K % kGemmBK == 0;
@@ -651,13 +724,18 @@ int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t strea
   const int rows = m1 * kTileL;
   if (m1 <= 0 || rows >= g.M) return launch_gemm<SCHED, E>(g, kTileL, epi, stream);
   a.M = rows;
+  a.a_rows = g.a_rows < rows ? g.a_rows : rows;
   a.tiles_m = m1;
   b.A = g.A + static_cast<int64_t>(rows) * g.lda;
   b.M = g.M - rows;
+  b.a_rows = g.a_rows > rows ? g.a_rows - rows : 0;
   b.tiles_m = (b.M + kTileS - 1) / kTileS;
   b.tiles_n = (g.N + kTileS - 1) / kTileS;
   a.at_cols = g.at_cols < rows ? g.at_cols : rows;
-  if (g.at_out != nullptr) b.at_out = g.at_out + rows;
+  // (packed: rows is a whole number of K steps of the packed A^T)
+  if (g.at_out != nullptr)
+    b.at_out = g.at_out + (g.at_pk_ks > 0 ? static_cast<int64_t>(rows / kGemmBK) * (kPackedStepBytes / 2)
+                                          : static_cast<int64_t>(rows));
   b.at_cols = g.at_cols > rows ? g.at_cols - rows : 0;
   b.bt_out = nullptr;
   int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
@@ -684,6 +762,7 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.ldb = ldb;
   g.M = M;
   g.N = N;
+  g.a_rows = M;
   g.b_rows = b_rows;
   g.K = K;
   g.tiles_m = (M + kTile - 1) / kTile;
@@ -696,6 +775,7 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.at_out = nullptr;
   g.ld_at = 0;
   g.at_cols = 0;
+  g.at_pk_ks = 0;
   g.bt_out = nullptr;
   g.ld_bt = 0;
   g.bt_cols = 0;
@@ -856,6 +936,7 @@ int grad_weight_product(const uint16_t* gt, const uint16_t* xtp, int64_t ldk, in
     if (tp.ksplit > 1) {
       GemmShape a = gs;
       a.M = tp.rows0;
+      a.a_rows = tp.rows0;
       a.tiles_m = tp.rows0 / kTileL;
       int st = launch_gemm<1, E>(a, kTileL, e, stream);
       if (st != LMX_OK) return st;
@@ -972,10 +1053,10 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.z_off = take(generic ? 0 : static_cast<size_t>(C) * w.ldv * 2);
   w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldk * 2);
   // packed copies (gemm.h) of the products' B operands: X^T [D, ldk], W^T
-  // [D, ldv] and, for the fused path's logits, W [V, D]
+  // [D, ldv] and, for the fused path's logits, the chunk's X_c [C, D]
   w.xt_off = take(packed_bytes(D, w.ldk));
   w.wt_off = take(packed_bytes(D, w.ldv));
-  w.wp_off = take(generic ? 0 : packed_bytes(V, D));
+  w.xp_off = take(generic ? 0 : packed_bytes(C, D));
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
   w.dw_off = take(accum == LMX_ACC_F32 && nchunks > w.dw_group ? static_cast<size_t>(V) * D * 4
                                                                  : 0);
@@ -998,7 +1079,7 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + wl.gt_off);
   uint16_t* xtp = reinterpret_cast<uint16_t*>(ws + wl.xt_off);
   uint16_t* wtp = reinterpret_cast<uint16_t*>(ws + wl.wt_off);
-  uint16_t* wp = reinterpret_cast<uint16_t*>(ws + wl.wp_off);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws + wl.xp_off);
   float* dxp = reinterpret_cast<float*>(ws + wl.dxp_off);
   float* dw = reinterpret_cast<float*>(ws + wl.dw_off);
   float* dwp = reinterpret_cast<float*>(ws + wl.dwp_off);
@@ -1017,12 +1098,9 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return LMX_ERR_HIP;
     return finish_enqueue(row_loss, 0, n_ws, p.reduction, p.loss, stream);
   }
-  // packed copies of W (the logits products' B) and of W^T [D, ldv] (the
-  // grad_inputs products' B; rows of W past V give zero columns)
-  st = pack_rows(p.w, p.D, V, D, ks_d, wp, stream);
-  if (st != LMX_OK) return st;
-  st = pack_transposed(p.w, p.D, V, D, static_cast<int>(ldv), wtp, ks_v, 0, stream);
-  if (st != LMX_OK) return st;
+  // the packed W^T [D, ldv] (the grad_inputs products' B) is written by chunk
+  // 0's logits product, which loads every tile of W (rows of W past V read as
+  // zero and give the padding columns)
   const int64_t nchunks = (p.BT + p.chunk - 1) / p.chunk;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t r0 = c * p.chunk;
@@ -1030,22 +1108,31 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     const uint16_t* xc = p.x + r0 * p.D;
     const int64_t* tc = p.target + r0;
     const int64_t slot = c % grp;   // this chunk's columns in G^T and X^T
-    // 1. X_c^T, packed, as this chunk's K steps of the group's X^T
+    // 1. X_c packed (the logits product's B) and X_c^T packed, as this chunk's
+    // K steps of the group's X^T
+    st = pack_rows(xc, p.D, rows, D, ks_d, xp, stream);
+    if (st != LMX_OK) return st;
     st = pack_transposed(xc, p.D, rows, D, static_cast<int>(ldc), xtp, ks_k,
                          static_cast<int>(slot * ldc / kGemmBK), stream);
     if (st != LMX_OK) return st;
-    // 2. logits Z = X_c W^T over all ldv columns (columns >= V read zero rows of W)
+    // 2. logits Z = X_c W^T over all ldv columns, taken as Z^T = W X_c^T (tiles
+    // of W rows through LDS, written out transposed; rows of W past V read as
+    // zero and give the padding columns)
     {
-      const int tile = pick_tile(rows, ldv);
-      GemmShape g = make_shape(xc, p.D, p.w, p.D, rows, static_cast<int>(ldv), V, D, 1, tile);
-      g.Bp = wp;
+      const int tile = pick_tile(ldv, rows);
+      GemmShape g = make_shape(p.w, p.D, nullptr, 0, static_cast<int>(ldv), rows, rows, D, 1, tile);
+      g.a_rows = V;
+      g.Bp = xp;
       g.bp_ks = ks_d;
-      if (staged_ok(z, ldv, ldv)) {
-        EpiOut<E, false, kOutStaged> e{z, ldv, nullptr, 0, nullptr, 1};
+      if (c == 0) {
+        g.at_out = wtp;
+        g.at_pk_ks = ks_v;
+        g.at_cols = static_cast<int>(ldv);
+        EpiOutT<E, true> e{z, ldv, static_cast<int>(ldv)};
         st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
                             : launch_gemm<1, E>(g, tile, e, stream);
       } else {
-        EpiOut<E> e{z, ldv, nullptr, 0, nullptr, 0};
+        EpiOutT<E, false> e{z, ldv, static_cast<int>(ldv)};
         st = tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
                             : launch_gemm<1, E>(g, tile, e, stream);
       }
