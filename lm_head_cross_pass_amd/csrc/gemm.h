@@ -32,6 +32,10 @@
 //   contiguous range of tiles (tiles that share A or B panels share an L2),
 //   whatever the grid size.
 //
+// gemm_nt_bdir_kernel (further down) keeps this structure for A and takes B
+// from a fragment-packed copy loaded straight into registers, so that only A
+// passes through LDS.
+//
 // The epilogue is a functor (see linear_ce.hip): init() sets the accumulators
 // before the K loop, run() stores them after it, and an epilogue with kRounds
 // also rounds them every round_every K steps (round_tile() on each MFMA tile).
