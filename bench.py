@@ -12,18 +12,15 @@ back, then their linear-CE calls, each part after its own warmup;
 * chunked linear-CE with inputs [16384, 4096] bf16 ~ N(0, 1), weight
   [128256, 4096] bf16 ~ N(0, 0.02), 2% ignored, chunk 2048, mean, z = 0,
   fp32 grad_weight accumulation, the library's default grad_weight grouping
-  (here one product over all eight chunks: their transposed logits gradient
-  fits 2 GiB plus the fp32 accumulator that one product does without).
+  (2 GiB of transposed logits gradient per product: four chunks).
 
 The JSON line reports the CE leg as ``value`` (GB/s of algorithmic traffic:
 one read of the logits, one write of the gradient, the int64 targets) with its
 roofline against the 8 TB/s HBM peak, and the linear-CE leg under
 ``linear_ce`` (TFLOP/s of the three matmuls, 6 BT V D, against the 2.5 PFLOP/s
 dense bf16 MFMA peak) with its workspace bytes, plus, each timed on its own,
-'weight' accumulation (its default: 2 GiB groups of four chunks), fp32 with an
-explicit 2 GiB budget (``fp32_2gib_groups``: two products and an fp32
-accumulator) and 'weight' with one product over every chunk
-(``weight_accum_one_group``: the G^T budget that holds all eight chunks).
+'weight' accumulation and both modes with one grad_weight product over every
+chunk (``one_group``: the G^T budget that holds all eight chunks).
 ``next_rows`` times the per-row entry points on the CE leg's logits (forward-only
 reduced CE, selective_log_softmax, the unreduced per-row CE and its VJP), each
 in GB/s of its own algorithmic bytes; ``linear_ce.generic_chunked_loss`` times the
@@ -124,9 +121,6 @@ def mean_median(ts):
     return sum(ts) / len(ts), statistics.median(ts)
 
 
-GIB2 = 1 << 31   # an explicit grad_weight group budget of 2 GiB
-
-
 def gt_group_bytes_all(BT: int, V: int, chunk: int) -> int:
     """A grad_weight group budget that covers every chunk of the call: the
     transposed logits gradient of all chunks (vocabulary padded to 256, chunk
@@ -204,8 +198,7 @@ def main() -> int:
             return _lib.linear_ce_workspace_bytes(lin_w.BT, lin_w.D, lin_w.V, _lib.LMX_BF16,
                                                   lin_w.chunk_size, accum, group_bytes)
         ws_bytes = max(lin_ws_bytes(_lib.LMX_ACC_F32), lin_ws_bytes(_lib.LMX_ACC_WEIGHT),
-                       lin_ws_bytes(_lib.LMX_ACC_F32, GIB2),
-                       lin_ws_bytes(_lib.LMX_ACC_WEIGHT, one_group))
+                       lin_ws_bytes(_lib.LMX_ACC_F32, one_group))
         lin_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
         def lin_call(accum, group_bytes=0):
@@ -303,13 +296,13 @@ def main() -> int:
                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": lin_traffic,
                             "algorithmic_flops_per_call": flops,
                             "mfma_busy": mfma_busy,
-                            "kernel": "whole linear_ce call (gemm_nt_bdir_kernel x3 per chunk + CE)"}}
-        # 'weight' accumulation (default budget), fp32 with an explicit 2 GiB
-        # budget (two grad_weight products and an fp32 accumulator), and 'weight'
-        # with one product over every chunk, each timed on its own
+                            "kernel": "whole linear_ce call (gemm_nt_kernel x3 per chunk + CE)"}}
+        # 'weight' accumulation, and both modes with one grad_weight product over
+        # every chunk (a G^T budget that holds them all: more workspace, no
+        # fp32 accumulator), each timed on its own
         if args.weight_steps > 0:
             for key, accum, gb in (("weight_accum", _lib.LMX_ACC_WEIGHT, 0),
-                                   ("fp32_2gib_groups", _lib.LMX_ACC_F32, GIB2),
+                                   ("one_group", _lib.LMX_ACC_F32, one_group),
                                    ("weight_accum_one_group", _lib.LMX_ACC_WEIGHT, one_group)):
                 wms, wmed = mean_median(per_call_ms(lambda: lin_call(accum, gb),
                                                     args.weight_steps, 1, stream))

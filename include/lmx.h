@@ -192,13 +192,10 @@ LMX_API int ce_fwd_bwd_noalloc(const void* logits, void* grad_logits, const int6
  *                 gradient of one grad_weight product may take: that product
  *                 covers as many chunks as that holds (at least one), and one
  *                 group's transposed gradient is all the workspace keeps of
- *                 it, whatever BT. 0 selects the default: 2 GiB, except that
- *                 in fp32 mode every chunk goes into one product when their
- *                 transposed gradient fits 2 GiB plus the bytes of the fp32
- *                 accumulator that one product does without (about the same
- *                 workspace). A larger budget means fewer grad_weight passes
- *                 (in fp32 mode, none over an fp32 accumulator once one group
- *                 takes every chunk) for more workspace; < 0 is LMX_ERR_SIZE.
+ *                 it, whatever BT. 0 selects the default, 2 GiB. A larger
+ *                 budget means fewer grad_weight passes (in fp32 mode, none
+ *                 over an fp32 accumulator once one group takes every chunk)
+ *                 for more workspace; < 0 is LMX_ERR_SIZE.
  *   loss          one fp32 on the device.
  *   grad_inputs   [BT, D] 16-bit output, 16-byte aligned.
  *   grad_weight   [V, D]  16-bit output, 16-byte aligned.

@@ -1035,11 +1035,6 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   if (nchunks > 1) {
     const int64_t per_chunk = w.ldv * w.ldc * 2;
     int64_t gsz = budget / per_chunk;
-    // the default budget in fp32 mode: all chunks in one product when their
-    // G^T fits the budget plus the fp32 accumulator that product does without
-    // (about the same workspace, one pass fewer over the accumulator)
-    if (group_bytes == 0 && accum == LMX_ACC_F32 && nchunks * per_chunk <= budget + V * D * 4)
-      gsz = nchunks;
     if (gsz > nchunks) gsz = nchunks;
     // the GEMM addresses 256 rows of G^T / X^T with 32-bit byte offsets
     const int64_t gmax = ((int64_t{1} << 31) - 1) / (256 * 2 * w.ldc);

@@ -94,19 +94,13 @@ def test_grad_weight_group_budget_bounds_the_workspace():
 
     def ws(BT, accum, budget):
         return _lib.linear_ce_workspace_bytes(BT, D, V, BF16, C, accum, budget)
-    # a 2 GiB budget (four chunks per product) does not grow with BT beyond the
-    # per-row loss terms
-    base = ws(16384, 0, 1 << 31)
-    assert ws(65536, 0, 1 << 31) - base <= (65536 - 16384) * 4 + 256
+    # the default budget (2 GiB: four chunks per product) does not grow with BT
+    # beyond the per-row loss terms
+    base = ws(16384, 0, 0)
+    assert ws(65536, 0, 0) - base <= (65536 - 16384) * 4 + 256
+    # the default is the 2 GiB budget given explicitly
+    assert ws(16384, 0, 1 << 31) == base
     xt_chunk = D * 2048 * 2
-    # the default in fp32 mode: every chunk in one product when their G^T fits
-    # 2 GiB plus the fp32 accumulator (8 chunks at BT = 16384), else the 2 GiB
-    # budget (32 chunks at BT = 65536)
-    assert ws(16384, 0, 0) == ws(16384, 0, 8 * gt_chunk)
-    assert ws(16384, 0, 0) - base <= 4 * xt_chunk + 4096
-    assert ws(65536, 0, 0) == ws(65536, 0, 1 << 31)
-    # weight-dtype mode: the default is the 2 GiB budget
-    assert ws(16384, 1, 0) == ws(16384, 1, 1 << 31)
     # fp32 mode: one product over all 8 chunks keeps no fp32 accumulator but
     # holds 4 more chunks of G^T and X^T
     one = ws(16384, 0, 8 * gt_chunk)
@@ -115,7 +109,7 @@ def test_grad_weight_group_budget_bounds_the_workspace():
     small = ws(16384, 0, gt_chunk)
     assert 3 * gt_chunk <= base - small <= 3 * (gt_chunk + xt_chunk) + (64 << 20)
     # weight-dtype mode keeps no fp32 accumulator
-    assert ws(16384, 1, 1 << 31) <= base - acc32
+    assert ws(16384, 1, 0) <= base - acc32
 
 
 def test_chunk_rows():
