@@ -296,7 +296,7 @@ def main() -> int:
                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": lin_traffic,
                             "algorithmic_flops_per_call": flops,
                             "mfma_busy": mfma_busy,
-                            "kernel": "whole linear_ce call (gemm_nt_kernel x3 per chunk + CE)"}}
+                            "kernel": "whole linear_ce call (gemm_nt_bdir_kernel x3 per chunk + CE)"}}
         # 'weight' accumulation, and both modes with one grad_weight product over
         # every chunk (a G^T budget that holds them all: more workspace, no
         # fp32 accumulator), each timed on its own

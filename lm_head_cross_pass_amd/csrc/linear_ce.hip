@@ -25,11 +25,12 @@
 // Finally the fixed-order loss reduction. In 'fp32' accumulation step 6 runs
 // once per group of chunks, on the group's columns of G^T and X^T together
 // (K = group ldc, ldk = group ldc; a last, partial group runs on the chunks it
-// has): as many chunks as 2 GiB of G^T holds (four at a vocabulary of 128256
-// and chunks of 2048), with dW in an fp32 workspace that the last product's
-// epilogue rounds to 16 bits, or all chunks in one product that writes the
-// 16-bit result directly when their G^T fits that budget plus the fp32
-// accumulator's bytes (16384 rows of 4096 at that vocabulary). In
+// has): as many chunks as the caller's budget of G^T holds (by default 2 GiB:
+// four at a vocabulary of 128256 and chunks of 2048), with dW in an fp32
+// workspace that the last product's epilogue rounds to 16 bits, or, when one
+// group takes every chunk, one product that writes the 16-bit result directly
+// with no fp32 accumulator. The budget bounds the G^T the workspace holds, so
+// the chunked path never keeps the whole batch's logits gradient. In
 // 'weight' accumulation the gradient is rounded to the 16-bit format after
 // every chunk, as the accumulation mode prescribes: a group's product rounds
 // its running sums at each chunk boundary of its K range, and the next group

@@ -153,9 +153,7 @@ def linear_ce(inputs: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
     """One library call: (loss, grad_inputs, grad_weight, n_valid, bad_target).
 
     ``group_bytes`` bounds the workspace bytes of transposed logits gradient
-    that one grad_weight product covers (None: the library's default, 2 GiB, or
-    in fp32 mode every chunk at once when their transposed gradient fits 2 GiB
-    plus the fp32 accumulator that one product does without)."""
+    that one grad_weight product covers (None: the library's default, 2 GiB)."""
     for t, n in ((inputs, "inputs"), (weight, "weight")):
         _require_device(t, n)
         if t.dim() != 2 or not t.is_contiguous():
