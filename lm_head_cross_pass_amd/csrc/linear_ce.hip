@@ -512,65 +512,60 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
-// Packed copy (the fragment-packed B layout of gemm.h) of M [R, K], row
-// stride ld, K a multiple of 8, with KS K steps per 32-row block. Block
-// (b, y) writes steps 4y .. 4y + 3 of row block b; thread t reads 16 bytes
-// (8 k values) of row t / 8 of the block, piece t % 8 of the step.
-__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restrict__ src,
-                                                        int64_t ld, int R, int K,
-                                                        uint16_t* __restrict__ dst, int KS) {
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int rl = tid >> 3, piece = tid & 7;
-  const int r = b * kPackedRows + rl;
-  // piece p holds k 8p .. 8p + 7 of the step: slice p / 2, lane half p % 2
-  const int lane = rl + 32 * (piece & 1), q = piece >> 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = blockIdx.y * 4 + i;
-    if (s >= KS) break;
-    const int k = s * kGemmBK + 8 * piece;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < R && k < K) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + k);
-    *reinterpret_cast<u32x4*>(dst + ((static_cast<int64_t>(b) * KS + s) * 4 + q) * 512 + lane * 8) =
-        v;
-  }
-}
-
-// Packed copy of S^T for S [R, Cs] (row stride ld, Cs a multiple of 8): the
-// packed rows are the columns of S and its K runs over the rows of S, zero
-// for rows R .. 64 gridDim.y - 1. Block (c, y) fills K step s_off + y of
-// column block c (KS steps per block) from a 64 x 32 tile of S through LDS.
-__global__ __launch_bounds__(256) void pack_transposed_kernel(const uint16_t* __restrict__ src,
-                                                              int64_t ld, int R, int Cs,
-                                                              uint16_t* __restrict__ dst, int KS,
-                                                              int s_off) {
-  __shared__ uint16_t t[64][kPackedRows + 2];
-  const int cb = blockIdx.x, y = blockIdx.y;
+// The packed copies (the fragment-packed B layout of gemm.h) of S [R, Cs]
+// (row stride ld, Cs a multiple of 8) from one read of each 64 x 64 tile of S:
+// rows_out, when given, gets S itself (blocks of 32 rows, K steps of 64
+// columns, KS_r steps per block, rows of the first nb_rows blocks), t_out,
+// when given, gets S^T (blocks of 32 columns of S, K running over the rows of
+// S: step s_off + y of a buffer with KS_t steps per block, blocks below
+// nb_cols). Elements past R or Cs are zeros. Block (y, c) takes rows 64 y .. +
+// 63 and columns 64 c .. + 63 (the row steps on grid x, the wider range).
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ src, int64_t ld,
+                                                   int R, int Cs, uint16_t* __restrict__ rows_out,
+                                                   int KS_r, int nb_rows,
+                                                   uint16_t* __restrict__ t_out, int KS_t,
+                                                   int s_off, int nb_cols) {
+  // rows padded by one 16-byte piece: the column gathers of the half-waves
+  // (rows 8 apart) land in different banks
+  __shared__ __align__(16) uint16_t t[64][64 + 8];
+  const int y = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
   {
-    const int rr = tid >> 2, cc = (tid & 3) * 8;
-    const int r = y * 64 + rr, c = cb * kPackedRows + cc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < R && c < Cs) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + c);
+    const int rr = tid >> 2, cc = (tid & 3) * 16;
+    const int r = y * 64 + rr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[rr][cc + 2 * e] = static_cast<uint16_t>(v[e] & 0xffffu);
-      t[rr][cc + 2 * e + 1] = static_cast<uint16_t>(v[e] >> 16);
+    for (int h = 0; h < 2; ++h) {
+      const int col = c * 64 + cc + 8 * h;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < R && col < Cs)
+        v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + col);
+      *reinterpret_cast<u32x4*>(&t[rr][cc + 8 * h]) = v;
     }
   }
   __syncthreads();
-  {
-    // lane l of slice q: column l & 31, rows 16 q + 8 (l >> 5) .. + 7
-    const int q = tid >> 6, l = tid & 63;
-    const int cl = l & 31, rb = 16 * q + 8 * (l >> 5);
-    u32x4 v;
+  // two output pieces per thread for each copy: w = (block half b, slice q, lane l)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = static_cast<uint32_t>(t[rb + 2 * e][cl]) |
-             (static_cast<uint32_t>(t[rb + 2 * e + 1][cl]) << 16);
-    *reinterpret_cast<u32x4*>(
-        dst + ((static_cast<int64_t>(cb) * KS + s_off + y) * 4 + q) * 512 + l * 8) = v;
+  for (int i = 0; i < 2; ++i) {
+    const int w = tid + 256 * i;                // 0 .. 511
+    const int b = w >> 8, q = (w >> 6) & 3, l = w & 63;
+    const int lr = l & 31, k0 = 16 * q + 8 * (l >> 5);
+    if (rows_out != nullptr && 2 * y + b < nb_rows) {
+      // row 32 b + lr of the tile, columns k0 .. k0 + 7
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&t[32 * b + lr][k0]);
+      *reinterpret_cast<u32x4*>(
+          rows_out + ((static_cast<int64_t>(2 * y + b) * KS_r + c) * 4 + q) * 512 + l * 8) = v;
+    }
+    if (t_out != nullptr && 2 * c + b < nb_cols) {
+      // column 32 b + lr of the tile, rows k0 .. k0 + 7
+      const int cl = 32 * b + lr;
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = static_cast<uint32_t>(t[k0 + 2 * e][cl]) |
+               (static_cast<uint32_t>(t[k0 + 2 * e + 1][cl]) << 16);
+      *reinterpret_cast<u32x4*>(
+          t_out + ((static_cast<int64_t>(2 * c + b) * KS_t + s_off + y) * 4 + q) * 512 + l * 8) = v;
+    }
   }
 }
 
@@ -802,24 +797,19 @@ size_t packed_bytes(int64_t rows, int64_t k) {
          kPackedStepBytes;
 }
 
-// Packed copy of M [R, K] (row stride ld) with KS steps per block.
-int pack_rows(const uint16_t* src, int64_t ld, int R, int K, int KS, uint16_t* dst,
-              hipStream_t stream) {
-  if (R == 0 || KS == 0) return LMX_OK;
-  dim3 grid((R + kPackedRows - 1) / kPackedRows, (KS + 3) / 4);
-  hipLaunchKernelGGL(pack_rows_kernel, grid, dim3(256), 0, stream, src, ld, R, K, dst, KS);
-  return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
-}
-
-// Packed copy of S^T for S [R, Cs] (row stride ld): K steps s_off .. s_off +
-// Rp / 64 - 1 of a packed buffer with KS steps per block (rows R .. Rp - 1 of
-// S read as zero; Rp a multiple of 64).
-int pack_transposed(const uint16_t* src, int64_t ld, int R, int Cs, int Rp, uint16_t* dst, int KS,
-                    int s_off, hipStream_t stream) {
+// Packed copies of S [R, Cs] (row stride ld): rows_out (when given) gets S
+// with KS_r = ceil(Cs / 64) steps per block, the blocks of its first R rows;
+// t_out (when given) gets S^T at K steps s_off .. s_off + Rp / 64 - 1 of a
+// buffer with KS_t steps per block (rows R .. Rp - 1 of S read as zero; Rp a
+// multiple of 64).
+int pack(const uint16_t* src, int64_t ld, int R, int Cs, int Rp, uint16_t* rows_out,
+         uint16_t* t_out, int KS_t, int s_off, hipStream_t stream) {
   if (Rp == 0 || Cs == 0) return LMX_OK;
-  dim3 grid((Cs + kPackedRows - 1) / kPackedRows, Rp / kGemmBK);
-  hipLaunchKernelGGL(pack_transposed_kernel, grid, dim3(256), 0, stream, src, ld, R, Cs, dst, KS,
-                     s_off);
+  const int ks_r = static_cast<int>(packed_steps(Cs));
+  dim3 grid(Rp / kGemmBK, ks_r);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, src, ld, R, Cs, rows_out, ks_r,
+                     (R + kPackedRows - 1) / kPackedRows, t_out, KS_t, s_off,
+                     (Cs + kPackedRows - 1) / kPackedRows);
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
@@ -1111,10 +1101,8 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     const int64_t slot = c % grp;   // this chunk's columns in G^T and X^T
     // 1. X_c packed (the logits product's B) and X_c^T packed, as this chunk's
     // K steps of the group's X^T
-    st = pack_rows(xc, p.D, rows, D, ks_d, xp, stream);
-    if (st != LMX_OK) return st;
-    st = pack_transposed(xc, p.D, rows, D, static_cast<int>(ldc), xtp, ks_k,
-                         static_cast<int>(slot * ldc / kGemmBK), stream);
+    st = pack(xc, p.D, rows, D, static_cast<int>(ldc), xp, xtp, ks_k,
+              static_cast<int>(slot * ldc / kGemmBK), stream);
     if (st != LMX_OK) return st;
     // 2. logits Z = X_c W^T over all ldv columns, taken as Z^T = W X_c^T (tiles
     // of W rows through LDS, written out transposed; rows of W past V read as
@@ -1207,13 +1195,12 @@ int linear_loss_grads_run(const LinearLossChunk& p, void* ws_base, hipStream_t s
   const int64_t slot = p.index % grp;   // this chunk's columns in G^T and X^T
   int st;
   if (p.index == 0) {   // packed W^T for every chunk of the pass
-    st = pack_transposed(p.w, p.D, V, D, static_cast<int>(ldv), wtp,
-                         static_cast<int>(packed_steps(ldv)), 0, stream);
+    st = pack(p.w, p.D, V, D, static_cast<int>(ldv), nullptr, wtp,
+              static_cast<int>(packed_steps(ldv)), 0, stream);
     if (st != LMX_OK) return st;
   }
-  st = pack_transposed(p.xc, p.D, p.rows, D, static_cast<int>(ldc), xtp,
-                       static_cast<int>(packed_steps(ldk)), static_cast<int>(slot * ldc / kGemmBK),
-                       stream);
+  st = pack(p.xc, p.D, p.rows, D, static_cast<int>(ldc), nullptr, xtp,
+            static_cast<int>(packed_steps(ldk)), static_cast<int>(slot * ldc / kGemmBK), stream);
   if (st != LMX_OK) return st;
   const bool fuse_gt = p.rows == p.chunk;   // G^T from the grad_inputs product
   if (!fuse_gt) {
