@@ -88,8 +88,8 @@ struct GemmShape {
   int tiles_m, tiles_n;
   int ksplit;            // number of K splits (1 = none)
   int ksteps_per_split;  // K steps per split
-  // Optional (at_out != nullptr; only for epilogues with kTransposes): every A
-  // tile also written out transposed,
+  // Optional (at_out != nullptr; gemm_nt_bdir_kernel with an epilogue that has
+  // kTransposes): every A tile also written out transposed,
   // at_out[k * ld_at + m] = A[m][k] for k < K, by one of the tiles_n
   // workgroups that load it (the one whose tile_n is the K step modulo
   // tiles_n); columns m >= at_cols are left alone. Rows of A past M read as
@@ -101,11 +101,6 @@ struct GemmShape {
   // (layout below) of A^T, whose rows are A's K and whose K runs over A's rows,
   // with at_pk_ks K steps per block; ld_at is then unused.
   int at_pk_ks;
-  // The same for B (bt_out[k * ld_bt + n] = B[n][k], columns n < bt_cols), by
-  // the one of the tiles_m workgroups whose tile_m is the K step modulo tiles_m.
-  uint16_t* bt_out;
-  int64_t ld_bt;
-  int bt_cols;
   // K steps between two roundings of the accumulators by the epilogue (its
   // round_tile(); only epilogues with kRounds), 0 for none: the weight-dtype
   // accumulation of grad_weight, one rounding per chunk of the K range.
@@ -477,17 +472,6 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
-      }
-    }
-    if constexpr (Epi::kTransposes) {
-      if (g.at_out != nullptr && ks % g.tiles_n == tn) {
-        gemm_store_tile_transposed<C, BM>(smem + cur_bytes, g.at_out, g.ld_at, m0, g.at_cols,
-                                          ks * kGemmBK, g.K);
-      }
-      if (g.bt_out != nullptr && ks % g.tiles_m == tm) {
-        static_assert(C::A_STAGE == C::B_STAGE, "B stages addressed with the A stage offset");
-        gemm_store_tile_transposed<C, BN>(smem + C::B_BASE + cur_bytes, g.bt_out, g.ld_bt, n0,
-                                          g.bt_cols, ks * kGemmBK, g.K);
       }
     }
     if (ks + 1 < ke) {

@@ -80,7 +80,7 @@ inline int staged_ok(const void* out, int64_t ld, int64_t n) {
 constexpr int kOutAny = 0, kOutStaged = 1, kOutPartial = 2;
 
 // TR: the product may also store one of its operands transposed (GemmShape's
-// at_out / bt_out); products that never do, or whose output mode is fixed,
+// at_out); products that never do, or whose output mode is fixed,
 // are compiled without the code they do not use.
 template <typename E, bool TR = false, int MODE = kOutAny>
 struct EpiOut {
@@ -628,12 +628,10 @@ template <int SCHED, typename E, typename Epi>
 int launch_gemm(const GemmShape& g, int tile, const Epi& epi, hipStream_t stream) {
   // an epilogue compiled without the transposed stores must not be given one
   // to do (no caller does; this keeps a future one from dropping them)
-  if (!Epi::kTransposes && (g.at_out != nullptr || g.bt_out != nullptr)) return LMX_ERR_UNSUPPORTED;
+  if (!Epi::kTransposes && g.at_out != nullptr) return LMX_ERR_UNSUPPORTED;
   if (!epi.mode_fits(g)) return LMX_ERR_UNSUPPORTED;
-  // a packed B never sits in LDS, so it cannot be written out transposed; a
-  // packed A^T is written by the packed-B kernel only
-  if (g.Bp != nullptr && g.bt_out != nullptr) return LMX_ERR_UNSUPPORTED;
-  if (g.Bp == nullptr && g.at_out != nullptr && g.at_pk_ks > 0) return LMX_ERR_UNSUPPORTED;
+  // the transposed A tiles are written by the packed-B kernel only
+  if (g.Bp == nullptr && g.at_out != nullptr) return LMX_ERR_UNSUPPORTED;
   const int blocks = g.tiles_m * g.tiles_n * g.ksplit;
   if (blocks == 0) return LMX_OK;
   const bool fullk = g.K % kGemmBK == 0;
@@ -706,12 +704,8 @@ int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t strea
     b.b_rows = g.b_rows > cols ? g.b_rows - cols : 0;
     b.tiles_m = (g.M + kTileS - 1) / kTileS;
     b.tiles_n = (b.N + kTileS - 1) / kTileS;
-    // transposed copies: A's whole tile rows are in both launches (the first
-    // writes them); B's columns continue in the second
+    // transposed A: A's whole tile rows are in both launches (the first writes them)
     b.at_out = nullptr;
-    a.bt_cols = g.bt_cols < cols ? g.bt_cols : cols;
-    if (g.bt_out != nullptr) b.bt_out = g.bt_out + cols;
-    b.bt_cols = g.bt_cols > cols ? g.bt_cols - cols : 0;
     int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
     if (st != LMX_OK) return st;
     return launch_gemm<SCHED, E>(b, kTileS, epi.shifted(0, cols), stream);
@@ -733,7 +727,6 @@ int launch_gemm_split_tail(const GemmShape& g, const Epi& epi, hipStream_t strea
     b.at_out = g.at_out + (g.at_pk_ks > 0 ? static_cast<int64_t>(rows / kGemmBK) * (kPackedStepBytes / 2)
                                           : static_cast<int64_t>(rows));
   b.at_cols = g.at_cols > rows ? g.at_cols - rows : 0;
-  b.bt_out = nullptr;
   int st = launch_gemm<SCHED, E>(a, kTileL, epi, stream);
   if (st != LMX_OK) return st;
   return launch_gemm<SCHED, E>(b, kTileS, epi.shifted(rows, 0), stream);
@@ -772,9 +765,6 @@ GemmShape make_shape(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
   g.ld_at = 0;
   g.at_cols = 0;
   g.at_pk_ks = 0;
-  g.bt_out = nullptr;
-  g.ld_bt = 0;
-  g.bt_cols = 0;
   g.round_every = 0;
   g.Bp = nullptr;
   g.bp_ks = 0;
