@@ -239,15 +239,34 @@ def test_grouped_products_with_k_split_tail_sampled():
 
 
 def test_split_tail_along_rows():
-    # one chunk of 8448 rows at V = 2048: its logits product has 33 x 8 large
-    # tiles, so the last 256 rows go to a second launch on small tiles (the
-    # split along the dimension with more tiles); the first launch alone
-    # writes W^T for grad_inputs
+    # one chunk of 8448 rows at V = 2048: its logits product (taken as
+    # W X_c^T) has 8 x 33 large tiles, so the last 256 token rows go to a
+    # second launch on small tiles (the split along the dimension with more
+    # tiles); the first launch alone writes the packed W^T for grad_inputs
     BT, D, V = 8448, 64, 2048
     X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=40, seed=43)
     loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, BT, "fp32")
     ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, block_rows=1024)
     assert int(n) == BT - 40 and int(bad) == 0
+    assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
+    assert _rel(gx, ref["grad_inputs"]) <= 1e-2
+    assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+@pytest.mark.parametrize("accum", ("fp32", "weight"))
+def test_logits_split_tail_along_vocabulary_rows(accum):
+    # V = 76800 (300 tile rows of W) and chunks of 256 rows (one tile column):
+    # chunk 0's logits product runs its first 256 tile rows as one launch and
+    # the last 11264 vocabulary rows on small tiles, and both launches write
+    # their part of the packed W^T; D = 200 is no multiple of 32 (the packed
+    # operands' last block and K step are part zeros) and the third chunk is
+    # ragged (88 rows)
+    BT, D, V, C = 600, 200, 76800, 256
+    X, W, t = workloads.small_linear_ce(BT, D, V, n_ignored=30, seed=61)
+    ref = oracle.linear_cross_entropy(X, W, t, -100, "mean", 1e-4, accum, chunk_size=C,
+                                      block_rows=200)
+    loss, gx, gw, n, bad = _run(X, W, t, "mean", 1e-4, C, accum)
+    assert int(n) == BT - 30 and int(bad) == 0
     assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
     assert _rel(gx, ref["grad_inputs"]) <= 1e-2
     assert _rel(gw, ref["grad_weight"]) <= 1e-2
