@@ -686,6 +686,21 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kerne
                           __builtin_amdgcn_readfirstlane((ks + 1 < ke ? ks + 1 : ks) * kGemmBK),
                           (t + 1) & 1, wave, g.K);
     __builtin_amdgcn_sched_barrier(0);
+    // this step's A tile written out transposed, when this workgroup's turn:
+    // at the start of the step, so the stores are older than the step's B
+    // loads (the waits for those never wait for the stores) and the other
+    // wave on each SIMD keeps the matrix core busy meanwhile
+    if constexpr (Epi::kTransposes) {
+      if (g.at_out != nullptr && ks % g.tiles_n == tn) {
+        if (g.at_pk_ks > 0)
+          gemm_store_tile_packed_t<C, BM>(smem + cur, g.at_out, g.at_pk_ks, m0, g.at_cols,
+                                          ks * kGemmBK, g.K);
+        else
+          gemm_store_tile_transposed<C, BM>(smem + cur, g.at_out, g.ld_at, m0, g.at_cols,
+                                            ks * kGemmBK, g.K);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // B of step ks + 1, slice by slice as each slice's registers free up (the
     // last step reloads its own: in bounds and unused)
     const int sn = __builtin_amdgcn_readfirstlane((ks + 1 < ke ? ks + 1 : ks) * kPackedStepBytes);
@@ -713,16 +728,6 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kerne
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
-      }
-    }
-    if constexpr (Epi::kTransposes) {
-      if (g.at_out != nullptr && ks % g.tiles_n == tn) {
-        if (g.at_pk_ks > 0)
-          gemm_store_tile_packed_t<C, BM>(smem + cur, g.at_out, g.at_pk_ks, m0, g.at_cols,
-                                          ks * kGemmBK, g.K);
-        else
-          gemm_store_tile_transposed<C, BM>(smem + cur, g.at_out, g.ld_at, m0, g.at_cols,
-                                            ks * kGemmBK, g.K);
       }
     }
     if (ks + 1 < ke) {
