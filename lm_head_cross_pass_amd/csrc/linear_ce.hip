@@ -4,11 +4,13 @@
 // page, "chunked_linear_loss" and "chunked_linear_cross_entropy").
 //
 // Per call:   count valid targets (global N, needed before any gradient is
-//             scaled); the packed copies (gemm.h) of W and of W^T [D, ldv]
-//             (zero-padded), the B operands of steps 2 and 5.
+//             scaled).
 // Per chunk of C rows (r0 .. r0 + C'):
-//   1. X_c^T into its K steps of the packed X^T [D, ldk]  pack
-//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM
+//   1. X_c packed (gemm.h) as step 2's B operand, and    pack
+//      X_c^T into its K steps of the packed X^T [D, ldk]
+//   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM, taken as
+//      Z^T = W X_c^T (W through LDS); chunk 0's also writes the packed
+//      W^T [D, ldv] (zero-padded), step 5's B operand
 //   3. the cross-entropy row kernel on Z, in place: loss terms and the
 //      gradient of the summed loss, G = (1 + 2 z lse) softmax - onehot
 //                                                      same kernel as ce_fwd_bwd
@@ -29,8 +31,8 @@
 // four at a vocabulary of 128256 and chunks of 2048), with dW in an fp32
 // workspace that the last product's epilogue rounds to 16 bits, or, when one
 // group takes every chunk, one product that writes the 16-bit result directly
-// with no fp32 accumulator. The budget bounds the G^T the workspace holds, so
-// the chunked path never keeps the whole batch's logits gradient. In
+// with no fp32 accumulator. The budget bounds the G^T the workspace holds (the
+// default keeps it well below the whole batch's logits gradient). In
 // 'weight' accumulation the gradient is rounded to the 16-bit format after
 // every chunk, as the accumulation mode prescribes: a group's product rounds
 // its running sums at each chunk boundary of its K range, and the next group
