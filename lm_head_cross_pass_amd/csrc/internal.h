@@ -89,7 +89,7 @@ struct LinearCeWorkspace {
   int64_t ldc;              // padded chunk-row stride of the transposed buffers
   int64_t ksplit;           // K splits of the grad_inputs GEMM
   int64_t dw_group;         // chunks per grad_weight product (as many as the G^T budget holds)
-  int64_t ldk;              // row stride of G^T and X_c^T: dw_group * ldc
+  int64_t ldk;              // K of a group: G^T's row stride, the packed X^T's K extent (dw_group * ldc)
   size_t n_valid_off, row_loss_off, z_off, gt_off, xt_off, wt_off, xp_off, dxp_off, dw_off,
       dwp_off, total;
   size_t dwp_bytes;         // K-split partials of grad_weight's last rows (0: none)
