@@ -230,12 +230,19 @@ LMX_API size_t linear_ce_workspace_bytes(int64_t BT, int64_t D, int64_t V, int d
  *   logits      [rows, ld_logits] 16-bit output (ld_logits >= V; columns >= V
  *               are not written), not overlapping the inputs; ld_logits is
  *               bounded like V (<= 4194048, LMX_ERR_SIZE beyond).
- * Limits as for linear_ce (LMX_ERR_SIZE); LMX_F32 is LMX_ERR_UNSUPPORTED. No
- * workspace.
+ *   workspace   >= linear_loss_logits_workspace_bytes(rows, D, dtype) bytes,
+ *               256-byte aligned (LMX_ERR_WORKSPACE otherwise; may be NULL
+ *               when rows is 0): the packed copy of inputs_c that the matmul
+ *               reads. Its contents on entry do not matter.
+ * Limits as for linear_ce (LMX_ERR_SIZE); LMX_F32 is LMX_ERR_UNSUPPORTED.
  */
 LMX_API int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows,
                                int64_t D, int64_t V, int dtype, void* logits,
-                               int64_t ld_logits, void* stream);
+                               int64_t ld_logits, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Workspace bytes linear_loss_logits needs (0 for invalid arguments). */
+LMX_API size_t linear_loss_logits_workspace_bytes(int64_t rows, int64_t D, int dtype);
 
 /*
  * linear_loss_grads -- gradients of one chunk of the generic chunked loss.

@@ -229,8 +229,15 @@ size_t linear_loss_workspace_bytes(int64_t BT, int64_t D, int64_t V, int dtype,
   return lmx::linear_ce_workspace_layout(BT, D, V, c, accum, true, 0).total;
 }
 
+size_t linear_loss_logits_workspace_bytes(int64_t rows, int64_t D, int dtype) {
+  if (rows < 0 || D <= 0 || D > kLinMaxD || rows > kLinMaxChunk) return 0;
+  if (dtype != LMX_BF16 && dtype != LMX_F16) return 0;
+  return lmx::linear_loss_logits_workspace(rows, D);
+}
+
 int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, int64_t D,
-                       int64_t V, int dtype, void* logits, int64_t ld_logits, void* stream) {
+                       int64_t V, int dtype, void* logits, int64_t ld_logits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (weight == nullptr || (rows > 0 && (inputs_c == nullptr || logits == nullptr)))
     return LMX_ERR_NULL;
   // the output's row stride is bounded like V: the GEMM epilogue addresses 256
@@ -247,11 +254,16 @@ int linear_loss_logits(const void* inputs_c, const void* weight, int64_t rows, i
   if (rows > 0 && (overlaps(logits, lb, inputs_c, static_cast<size_t>(rows) * D * 2) ||
                    overlaps(logits, lb, weight, static_cast<size_t>(V) * D * 2)))
     return LMX_ERR_ALIAS;
+  if (rows == 0) return LMX_OK;
+  if (workspace == nullptr) return LMX_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0 ||
+      workspace_bytes < lmx::linear_loss_logits_workspace(rows, D))
+    return LMX_ERR_WORKSPACE;
   return lmx::linear_loss_logits_enqueue(dtype, static_cast<const uint16_t*>(inputs_c),
                                          static_cast<const uint16_t*>(weight),
                                          static_cast<int>(rows), static_cast<int>(D),
                                          static_cast<int>(V), static_cast<uint16_t*>(logits),
-                                         ld_logits, static_cast<hipStream_t>(stream));
+                                         ld_logits, workspace, static_cast<hipStream_t>(stream));
 }
 
 int linear_loss_grads(const void* inputs_c, const void* weight, const void* grad_logits,

@@ -105,7 +105,10 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream);
 // Generic chunked linear loss (the caller's loss and logits gradient per chunk):
 // logits of one chunk, then its gradients.
 int linear_loss_logits_enqueue(int dtype, const uint16_t* xc, const uint16_t* w, int rows, int D,
-                               int V, uint16_t* logits, int64_t ld_logits, hipStream_t stream);
+                               int V, uint16_t* logits, int64_t ld_logits, void* ws,
+                               hipStream_t stream);
+// Workspace bytes of linear_loss_logits: the packed copy of the chunk's inputs.
+size_t linear_loss_logits_workspace(int64_t rows, int64_t D);
 struct LinearLossChunk {
   int dtype;                // LMX_BF16 or LMX_F16
   const uint16_t* xc;       // [rows, D]

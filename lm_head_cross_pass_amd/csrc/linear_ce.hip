@@ -1160,10 +1160,33 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
   return finish_enqueue(row_loss, p.BT, n_ws, p.reduction, p.loss, stream);
 }
 
+size_t linear_loss_logits_workspace(int64_t rows, int64_t D) {
+  const size_t b = packed_bytes(rows, D);
+  return b > kWsAlign ? align_up(b, kWsAlign) : kWsAlign;
+}
+
+// The logits of one chunk of the generic loss into the caller's buffer. When
+// its rows take whole 16-byte pieces, as the fused path's logits: Z^T = W X_c^T
+// with W's tiles through LDS and the chunk's packed X_c (in ws) as the B
+// operand, each tile written out transposed (columns >= V untouched); else
+// X_c W^T with W through LDS too and element stores.
 template <typename E>
 int linear_loss_logits_run(const uint16_t* xc, const uint16_t* w, int rows, int D, int V,
-                           uint16_t* logits, int64_t ld_logits, hipStream_t stream) {
+                           uint16_t* logits, int64_t ld_logits, void* ws, hipStream_t stream) {
   if (rows == 0) return LMX_OK;
+  if (staged_ok(logits, ld_logits, V)) {
+    uint16_t* xp = static_cast<uint16_t*>(ws);
+    int st = pack(xc, D, rows, D, static_cast<int>(round_up64(rows, kGemmBK)), xp, nullptr, 0, 0,
+                  stream);
+    if (st != LMX_OK) return st;
+    const int tile = pick_tile(V, rows);
+    GemmShape g = make_shape(w, D, nullptr, 0, V, rows, rows, D, 1, tile);
+    g.Bp = xp;
+    g.bp_ks = static_cast<int>(packed_steps(D));
+    EpiOutT<E, false> e{logits, ld_logits, V};
+    return tile == kTileL ? launch_gemm_split_tail<1, E>(g, e, stream)
+                          : launch_gemm<1, E>(g, tile, e, stream);
+  }
   const int tile = pick_tile(rows, V);
   GemmShape g = make_shape(xc, D, w, D, rows, V, V, D, 1, tile);
   EpiOut<E> e{logits, ld_logits, nullptr, 0, nullptr, staged_ok(logits, ld_logits, V)};
@@ -1219,10 +1242,11 @@ int linear_ce_enqueue(const LinearCeParams& p, void* ws, hipStream_t stream) {
 }
 
 int linear_loss_logits_enqueue(int dtype, const uint16_t* xc, const uint16_t* w, int rows, int D,
-                               int V, uint16_t* logits, int64_t ld_logits, hipStream_t stream) {
+                               int V, uint16_t* logits, int64_t ld_logits, void* ws,
+                               hipStream_t stream) {
   return dtype == LMX_F16
-             ? linear_loss_logits_run<F16>(xc, w, rows, D, V, logits, ld_logits, stream)
-             : linear_loss_logits_run<Bf16>(xc, w, rows, D, V, logits, ld_logits, stream);
+             ? linear_loss_logits_run<F16>(xc, w, rows, D, V, logits, ld_logits, ws, stream)
+             : linear_loss_logits_run<Bf16>(xc, w, rows, D, V, logits, ld_logits, ws, stream);
 }
 
 int linear_loss_grads_enqueue(const LinearLossChunk& p, void* ws, hipStream_t stream) {

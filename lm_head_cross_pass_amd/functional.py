@@ -397,6 +397,7 @@ def chunked_linear_loss_fwd(inputs: torch.Tensor, weight: torch.Tensor, loss_and
     nbytes = _lib.linear_loss_workspace_bytes(BT, D, V, ldt, cs, acc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _workspace(nbytes, dev)
+    lws = _workspace(_lib.linear_loss_logits_workspace_bytes(C, D, ldt), dev)
     stream = _stream_handle(dev)
     with torch.cuda.device(dev):
         for ci, r0 in enumerate(range(0, BT, C)):
@@ -405,7 +406,7 @@ def chunked_linear_loss_fwd(inputs: torch.Tensor, weight: torch.Tensor, loss_and
             logits = torch.empty((rows, V), dtype=inputs.dtype, device=dev)
             _lib.check("linear_loss_logits", _lib.linear_loss_logits(
                 inputs[r0:r1].data_ptr(), weight.data_ptr(), rows, D, V, ldt,
-                logits.data_ptr(), V, stream))
+                logits.data_ptr(), V, lws.data_ptr(), lws.numel(), stream))
             args = [_slice_rows(a, BT, r0, r1) for a in loss_args]
             kwargs = {k: _slice_rows(v, BT, r0, r1) for k, v in loss_kwargs.items()}
             loss_c, g = loss_and_grad_fn(logits, *args, **kwargs)

@@ -34,7 +34,8 @@ def test_every_declared_function_is_exported():
                           "lmx_status_string", "lmx_copy", "lmx_stream_probe", "lmx_scale",
                           "selective_log_softmax",
                           "ce_loss_rows", "ce_loss_rows_vjp", "linear_loss_logits",
-                          "linear_loss_grads", "linear_loss_workspace_bytes"}
+                          "linear_loss_grads", "linear_loss_workspace_bytes",
+                          "linear_loss_logits_workspace_bytes"}
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -335,17 +336,38 @@ def test_noalloc_argument_errors():
 
 def test_linear_loss_logits_argument_errors():
     f = _lib.linear_loss_logits
-    assert f(A, None, 16, 64, 1000, BF16, A + (3 << 34), 1000, None) == _lib.LMX_ERR_NULL
-    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + (3 << 34), 999, None) == _lib.LMX_ERR_SIZE
+    O = A + (3 << 34)   # logits
+    assert f(A, None, 16, 64, 1000, BF16, O, 1000, None, 0, None) == _lib.LMX_ERR_NULL
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, O, 999, None, 0, None) == _lib.LMX_ERR_SIZE
     # an output stride beyond what 32-bit offsets over 256 rows reach
-    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + (3 << 34), 4194048 + 8,
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, O, 4194048 + 8, None, 0,
              None) == _lib.LMX_ERR_SIZE
-    assert f(A, A + (1 << 34), 16, 64, 1000, 7, A + (3 << 34), 1000, None) == _lib.LMX_ERR_ENUM
-    assert f(A, A + (1 << 34), 16, 60, 1000, BF16, A + (3 << 34), 1000, None) == _lib.LMX_ERR_ALIGN
-    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + 64, 1000, None) == _lib.LMX_ERR_ALIAS
-    assert f(None, A, 0, 64, 1000, BF16, None, 1000, None) == _lib.LMX_OK
+    assert f(A, A + (1 << 34), 16, 64, 1000, 7, O, 1000, None, 0, None) == _lib.LMX_ERR_ENUM
+    assert f(A, A + (1 << 34), 16, 60, 1000, BF16, O, 1000, None, 0, None) == _lib.LMX_ERR_ALIGN
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, A + 64, 1000, None, 0,
+             None) == _lib.LMX_ERR_ALIAS
+    assert f(None, A, 0, 64, 1000, BF16, None, 1000, None, 0, None) == _lib.LMX_OK
+    # the workspace holds the packed chunk inputs: required, aligned, big enough
+    need = _lib.linear_loss_logits_workspace_bytes(16, 64, BF16)
+    ws = A + (5 << 34)
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, O, 1000, None, need,
+             None) == _lib.LMX_ERR_NULL
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, O, 1000, ws + 64, need,
+             None) == _lib.LMX_ERR_WORKSPACE
+    assert f(A, A + (1 << 34), 16, 64, 1000, BF16, O, 1000, ws, need - 1,
+             None) == _lib.LMX_ERR_WORKSPACE
     assert _lib.linear_loss_workspace_bytes(64, 64, 1000, BF16, 16, 0) > 0
     assert _lib.linear_loss_workspace_bytes(64, 64, 1000, F32, 16, 0) == 0
+
+
+def test_linear_loss_logits_workspace_bytes():
+    # 32-row blocks of 64-wide K steps, 4 KiB each (the packed chunk inputs)
+    assert _lib.linear_loss_logits_workspace_bytes(2048, 4096, BF16) == 64 * 64 * 4096
+    assert _lib.linear_loss_logits_workspace_bytes(100, 72, _lib.LMX_F16) == 4 * 2 * 4096
+    assert _lib.linear_loss_logits_workspace_bytes(0, 64, BF16) > 0
+    assert _lib.linear_loss_logits_workspace_bytes(16, 64, F32) == 0
+    assert _lib.linear_loss_logits_workspace_bytes(-1, 64, BF16) == 0
+    assert _lib.linear_loss_logits_workspace_bytes(16, 0, BF16) == 0
 
 
 def test_header_is_plain_c_and_links(tmp_path):

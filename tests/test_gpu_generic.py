@@ -172,3 +172,44 @@ def test_split_tail_launches_generic(dtype):
     assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
     assert _rel(gx, ref["grad_inputs"]) <= 1e-2
     assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+@pytest.mark.parametrize("rows,D,V,ld,offset", [
+    (37, 64, 1000, 1000, 0),     # 16-byte rows: the packed product, staged stores
+    (300, 136, 2000, 2008, 0),   # staged, padding columns past V
+    (37, 64, 1001, 1001, 0),     # odd V: element stores through the LDS product
+    (130, 72, 777, 784, 0),      # odd V with padding columns
+    (300, 136, 1000, 1000, 1),   # logits two bytes past a 16-byte boundary
+])
+@pytest.mark.parametrize("dtype", (torch.bfloat16, torch.float16))
+def test_chunk_logits_through_the_c_abi(rows, D, V, ld, offset, dtype):
+    """linear_loss_logits called directly: every logit of the chunk against
+    inputs @ weight.T in fp64, element by element. The kernel's products of
+    16-bit operands are exact in fp32 and the fp32 sum over D errs by at most
+    D * 2^-24 * (|x| @ |w|^T); rounding to the output format then adds half an
+    ulp (2^-8 relative for bf16, 2^-11 for fp16). Columns past V keep their
+    sentinel."""
+    from lm_head_cross_pass_amd import _lib
+    X, W, _ = workloads.small_linear_ce(rows, D, V, dtype=dtype, seed=rows + V)
+    code = _lib.LMX_BF16 if dtype == torch.bfloat16 else _lib.LMX_F16
+    half_ulp = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    sentinel = -7.0
+    buf = torch.full((rows * ld + offset,), sentinel, dtype=dtype, device=DEV)
+    out = buf[offset:].view(rows, ld)
+    nbytes = _lib.linear_loss_logits_workspace_bytes(rows, D, code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    _lib.check("linear_loss_logits", _lib.linear_loss_logits(
+        Xd.data_ptr(), Wd.data_ptr(), rows, D, V, code, out.data_ptr(), ld,
+        ws.data_ptr(), nbytes, stream))
+    torch.cuda.synchronize()
+    got = out.double().cpu()
+    Xf, Wf = X.double(), W.double()
+    ref = Xf @ Wf.T
+    acc_err = D * 2.0 ** -24 * (Xf.abs() @ Wf.abs().T)
+    bound = acc_err + half_ulp * (ref.abs() + acc_err)
+    err = (got[:, :V] - ref).abs()
+    assert bool((err <= bound).all()), float((err - bound).max())
+    assert bool((got[:, V:] == sentinel).all())
+    assert bool((buf[:offset].double().cpu() == sentinel).all())
