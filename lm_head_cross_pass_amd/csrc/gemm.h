@@ -441,6 +441,11 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     __syncthreads();
     gemm_load_frags<C, 0>(smem, a_off, b_off, 0, fa0, fb0);
   }
+  // (ks + 1) % round_every, kept as a counter (the modulo of a runtime divisor
+  // costs some twenty scalar instructions a step)
+  [[maybe_unused]] int phase = 1;
+  if constexpr (Epi::kRounds)
+    if (g.round_every > 0) phase = __builtin_amdgcn_readfirstlane((kb + 1) % g.round_every);
   for (int ks = kb; ks < ke; ++ks) {
     const int t = ks - kb;
     const int cur_bytes = __builtin_amdgcn_readfirstlane((t % kGemmStages) * C::A_STAGE);
@@ -467,12 +472,13 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_kernel(Gem
     if constexpr (Epi::kRounds) {
       // a chunk boundary inside the K range: the epilogue rounds the running
       // sums (the last boundary is the epilogue's own rounding)
-      if (g.round_every > 0 && (ks + 1) % g.round_every == 0 && ks + 1 < ke) {
+      if (g.round_every > 0 && phase == 0 && ks + 1 < ke) {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
       }
+      if (++phase == g.round_every) phase = 0;
     }
     if (ks + 1 < ke) {
       // step ks + 1 landed: the copies issued after it (up to AHEAD - 1 steps)
@@ -677,6 +683,11 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kerne
     __syncthreads();
     gemm_load_a_frags<C, 0>(smem, a_off, 0, fa0);
   }
+  // (ks + 1) % round_every, kept as a counter (the modulo of a runtime divisor
+  // costs some twenty scalar instructions a step)
+  [[maybe_unused]] int phase = 1;
+  if constexpr (Epi::kRounds)
+    if (g.round_every > 0) phase = __builtin_amdgcn_readfirstlane((kb + 1) % g.round_every);
   for (int ks = kb; ks < ke; ++ks) {
     const int t = ks - kb;
     const int cur = __builtin_amdgcn_readfirstlane((t & 1) * C::A_STAGE);
@@ -723,12 +734,13 @@ __global__ __launch_bounds__(gemm_threads<BM * BN>(), 1) void gemm_nt_bdir_kerne
     gemm_load_b_slice<C, 3>(bc, rb, b_voff, sn);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (Epi::kRounds) {
-      if (g.round_every > 0 && (ks + 1) % g.round_every == 0 && ks + 1 < ke) {
+      if (g.round_every > 0 && phase == 0 && ks + 1 < ke) {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) epi.round_tile(acc[i][j]);
       }
+      if (++phase == g.round_every) phase = 0;
     }
     if (ks + 1 < ke) {
       // A of step ks + 1 landed (this step's B loads, issued after it, may
