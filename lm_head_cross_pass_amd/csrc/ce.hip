@@ -347,9 +347,11 @@ __device__ __forceinline__ void prefetch_to_lds(char* lds, const RowView& r, int
 // LDS as soon as the current row's sweep has read its own, so that part of
 // the next row streams in while this row's gradient is computed and stored;
 // the other CPT - PRE chunks are loaded into registers after the stores.
+// MINW > 1 bounds the registers so that MINW waves fit on each SIMD (more
+// workgroups resident per CU).
 template <typename T, int THREADS, int CPT, bool GRAD, bool BURST = (THREADS >= 1024),
-          int PRE = 0>
-__global__ __launch_bounds__(THREADS) void ce_rows_reg_kernel(CeParams p) {
+          int PRE = 0, int MINW = 1>
+__global__ __launch_bounds__(THREADS, MINW) void ce_rows_reg_kernel(CeParams p) {
   constexpr int EPC = Elem<T>::kPerChunk;
   constexpr int W = THREADS / 64;
   static_assert(PRE == 0 || (GRAD && BURST && PRE < CPT), "LDS prefetch with burst stores only");
@@ -751,22 +753,35 @@ struct RowKernel {
   const void* fn;
   int threads;
   int64_t capacity;  // chunks per row that fit; 0 = any (streaming)
+  // for at most kFewRowsPerCu rows per CU (nullptr: fn): the same rows in
+  // fewer registers, more workgroups resident per CU
+  const void* few_rows_fn;
 };
+
+// With few rows per CU each workgroup walks only one or two rows, so the
+// reads of a row are not overlapped with the stores of another within a
+// workgroup; three workgroups per CU instead of two put more rows in flight
+// at once. [1024, 50257] bf16 rows with their gradient (a chunk of the
+// 8192 x 768 x 50257 linear cross-entropy): 1.2% off the whole linear call;
+// [4096, 50257]: 2.5% slower than two per CU, so only up to 4 rows per CU.
+constexpr int64_t kFewRowsPerCu = 4;
 
 template <typename T, bool G>
 const RowKernel* row_kernels(int* count) {
   static const RowKernel k[] = {
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 1, G>), 256, 256},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 2, G>), 256, 512},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 4, G>), 256, 1024},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 8, G>), 256, 2048},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 16, G>), 256, 4096},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13, G>), 512, 6656},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 16, G>), 512, 8192},
-      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 12, G>), 1024, 12288},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 1, G>), 256, 256, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 2, G>), 256, 512, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 4, G>), 256, 1024, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 8, G>), 256, 2048, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 256, 16, G>), 256, 4096, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13, G>), 512, 6656,
+       G ? reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 13, G, false, 0, 6>)
+         : nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 512, 16, G>), 512, 8192, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 12, G>), 1024, 12288, nullptr},
       {reinterpret_cast<const void*>(&ce_rows_reg_kernel<T, 1024, 16, G, true, G ? 9 : 0>),
-       1024, 16384},
-      {reinterpret_cast<const void*>(&ce_rows_stream_kernel<T, 1024>), 1024, 0},
+       1024, 16384, nullptr},
+      {reinterpret_cast<const void*>(&ce_rows_stream_kernel<T, 1024>), 1024, 0, nullptr},
   };
   *count = static_cast<int>(sizeof(k) / sizeof(k[0]));
   return k;
@@ -782,14 +797,21 @@ int64_t ce_max_row_chunks(uintptr_t base, int64_t V, int64_t ld, int elem_bytes)
   return (epc - 1 + V + epc - 1) / epc;
 }
 
-// Workgroups of a row-kernel launch: as many as are resident on the chip, at
-// most one per row (each walks rows blockIdx, blockIdx + grid, ...).
-static int occupancy_grid(const void* fn, int threads, int64_t rows) {
+// Compute units of the current device (-1 on error).
+static int device_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return -1;
+  return cus;
+}
+
+// Workgroups of a row-kernel launch: as many as are resident on the chip, at
+// most one per row (each walks rows blockIdx, blockIdx + grid, ...).
+static int occupancy_grid(const void* fn, int threads, int64_t rows) {
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
     return -1;
@@ -826,11 +848,17 @@ int ce_rows_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
     for (int i = 0; i < n; ++i) {
       if (ks[i].capacity == 0 || ks[i].capacity >= need) { pick = &ks[i]; break; }
     }
-    const int grid = occupancy_grid(pick->fn, pick->threads, p.B);
+    const void* fn = pick->fn;
+    if (pick->few_rows_fn != nullptr) {
+      const int cus = device_cus();
+      if (cus <= 0) return LMX_ERR_HIP;
+      if (p.B <= kFewRowsPerCu * cus) fn = pick->few_rows_fn;
+    }
+    const int grid = occupancy_grid(fn, pick->threads, p.B);
     if (grid <= 0) return LMX_ERR_HIP;
     CeParams pc = p;
     void* args[] = {&pc};
-    if (hipLaunchKernel(pick->fn, dim3(grid), dim3(pick->threads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(fn, dim3(grid), dim3(pick->threads), args, 0, stream) != hipSuccess)
       return LMX_ERR_HIP;
   }
   return LMX_OK;

@@ -6,8 +6,9 @@
 // Per call:   count valid targets (global N, needed before any gradient is
 //             scaled).
 // Per chunk of C rows (r0 .. r0 + C'):
-//   1. X_c packed (gemm.h) as step 2's B operand, and    pack
-//      X_c^T into its K steps of the packed X^T [D, ldk]
+//   1. X_c packed (gemm.h) as step 2's B operand, and    pack, one launch for
+//      X_c^T into its K steps of the packed X^T [D, ldk]  every chunk of a
+//                                                      grad_weight group
 //   2. Z = X_c W^T, bf16, [C', ldv] (padding columns 0) MFMA GEMM, taken as
 //      Z^T = W X_c^T (W through LDS); chunk 0's also writes the packed
 //      W^T [D, ldv] (zero-padded), step 5's B operand
@@ -524,14 +525,26 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
 // 63 and columns 64 c .. + 63 (the row steps on grid x, the wider range).
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                    int R, int Cs, uint16_t* __restrict__ rows_out,
-                                                   int KS_r, int nb_rows,
-                                                   uint16_t* __restrict__ t_out, int KS_t,
-                                                   int s_off, int nb_cols) {
+                                                   int KS_r, uint16_t* __restrict__ t_out,
+                                                   int KS_t, int s_off, int nb_cols, int zrows,
+                                                   int64_t rows_out_z, int s_z) {
   // rows padded by one 16-byte piece: the column gathers of the half-waves
   // (rows 8 apart) land in different banks
   __shared__ __align__(16) uint16_t t[64][64 + 8];
   const int y = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
+  // slice z of the launch: rows z zrows .. of S, as a source of its own (rows
+  // past its zrows read as zero), packed rows_out_z elements further on and
+  // s_z K steps further on in the transposed copy
+  {
+    const int z = blockIdx.z;
+    const int64_t zr0 = static_cast<int64_t>(z) * zrows;
+    src += zr0 * ld;
+    R = R - static_cast<int>(zr0) < zrows ? R - static_cast<int>(zr0) : zrows;
+    if (rows_out != nullptr) rows_out += z * rows_out_z;
+    s_off += z * s_z;
+  }
+  const int nb_rows = (R + kPackedRows - 1) / kPackedRows;
   {
     const int rr = tid >> 2, cc = (tid & 3) * 16;
     const int r = y * 64 + rr;
@@ -794,14 +807,22 @@ size_t packed_bytes(int64_t rows, int64_t k) {
 // t_out (when given) gets S^T at K steps s_off .. s_off + Rp / 64 - 1 of a
 // buffer with KS_t steps per block (rows R .. Rp - 1 of S read as zero; Rp a
 // multiple of 64).
+// With nz > 1, one launch packs nz consecutive slices of zrows rows each (the
+// chunks of a grad_weight group; the last may be shorter, R counting the rows
+// of all of them) as nz such calls would: slice z's rows at rows_out + z
+// rows_out_z and its transpose at K steps s_off + z s_z .., each slice's rows
+// past zrows reading as zero up to Rp.
 int pack(const uint16_t* src, int64_t ld, int R, int Cs, int Rp, uint16_t* rows_out,
-         uint16_t* t_out, int KS_t, int s_off, hipStream_t stream) {
-  if (Rp == 0 || Cs == 0) return LMX_OK;
+         uint16_t* t_out, int KS_t, int s_off, hipStream_t stream, int nz = 1, int zrows = 0,
+         int64_t rows_out_z = 0, int s_z = 0) {
+  if (Rp == 0 || Cs == 0 || nz < 1) return LMX_OK;
+  if (nz == 1) zrows = R;
+  if (zrows < 1 || static_cast<int64_t>(nz - 1) * zrows >= R) return LMX_ERR_SIZE;
   const int ks_r = static_cast<int>(packed_steps(Cs));
-  dim3 grid(Rp / kGemmBK, ks_r);
+  dim3 grid(Rp / kGemmBK, ks_r, nz);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, src, ld, R, Cs, rows_out, ks_r,
-                     (R + kPackedRows - 1) / kPackedRows, t_out, KS_t, s_off,
-                     (Cs + kPackedRows - 1) / kPackedRows);
+                     t_out, KS_t, s_off, (Cs + kPackedRows - 1) / kPackedRows, zrows,
+                     rows_out_z, s_z);
   return hipGetLastError() == hipSuccess ? LMX_OK : LMX_ERR_HIP;
 }
 
@@ -1039,7 +1060,7 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   // [D, ldv] and, for the fused path's logits, the chunk's X_c [C, D]
   w.xt_off = take(packed_bytes(D, w.ldk));
   w.wt_off = take(packed_bytes(D, w.ldv));
-  w.xp_off = take(generic ? 0 : packed_bytes(C, D));
+  w.xp_off = take(generic ? 0 : w.dw_group * packed_bytes(C, D));
   w.dxp_off = take(w.ksplit > 1 ? static_cast<size_t>(w.ksplit) * C * D * 4 : 0);
   w.dw_off = take(accum == LMX_ACC_F32 && nchunks > w.dw_group ? static_cast<size_t>(V) * D * 4
                                                                  : 0);
@@ -1071,6 +1092,7 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
   const int64_t* mean_count = p.reduction == LMX_MEAN ? n_ws : nullptr;
   const int ks_d = static_cast<int>(packed_steps(D)), ks_v = static_cast<int>(packed_steps(ldv));
   const int ks_k = static_cast<int>(packed_steps(ldk));
+  const int64_t xp_chunk = static_cast<int64_t>(packed_bytes(p.chunk, p.D) / 2);   // elements
 
   int st = count_enqueue(p.target, p.BT, p.V, p.ignore_index, n_ws, p.n_valid_user, p.bad_user,
                          stream);
@@ -1091,11 +1113,17 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
     const uint16_t* xc = p.x + r0 * p.D;
     const int64_t* tc = p.target + r0;
     const int64_t slot = c % grp;   // this chunk's columns in G^T and X^T
-    // 1. X_c packed (the logits product's B) and X_c^T packed, as this chunk's
-    // K steps of the group's X^T
-    st = pack(xc, p.D, rows, D, static_cast<int>(ldc), xp, xtp, ks_k,
-              static_cast<int>(slot * ldc / kGemmBK), stream);
-    if (st != LMX_OK) return st;
+    // 1. at the group's first chunk, one launch for all its chunks: X_c packed
+    // (the logits product's B, one copy per chunk) and X_c^T packed, as the
+    // chunk's K steps of the group's X^T
+    if (slot == 0) {
+      const int64_t nz = grp < nchunks - c ? grp : nchunks - c;
+      const int64_t grows = p.BT - r0 < nz * p.chunk ? p.BT - r0 : nz * p.chunk;
+      st = pack(xc, p.D, static_cast<int>(grows), D, static_cast<int>(ldc), xp, xtp, ks_k, 0,
+                stream, static_cast<int>(nz), static_cast<int>(p.chunk), xp_chunk,
+                static_cast<int>(ldc / kGemmBK));
+      if (st != LMX_OK) return st;
+    }
     // 2. logits Z = X_c W^T over all ldv columns, taken as Z^T = W X_c^T (tiles
     // of W rows through LDS, written out transposed; rows of W past V read as
     // zero and give the padding columns)
@@ -1103,7 +1131,7 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
       const int tile = pick_tile(ldv, rows);
       GemmShape g = make_shape(p.w, p.D, nullptr, 0, static_cast<int>(ldv), rows, rows, D, 1, tile);
       g.a_rows = V;
-      g.Bp = xp;
+      g.Bp = xp + slot * xp_chunk;
       g.bp_ks = ks_d;
       if (c == 0) {
         g.at_out = wtp;

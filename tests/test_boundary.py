@@ -101,14 +101,16 @@ def test_grad_weight_group_budget_bounds_the_workspace():
     assert ws(65536, 0, 0) - base <= (65536 - 16384) * 4 + 256
     # the default is the 2 GiB budget given explicitly
     assert ws(16384, 0, 1 << 31) == base
+    # a chunk's packed X^T columns, and its packed X_c (the group's chunks are
+    # packed together, one copy per chunk of the group)
     xt_chunk = D * 2048 * 2
     # fp32 mode: one product over all 8 chunks keeps no fp32 accumulator but
-    # holds 4 more chunks of G^T and X^T
+    # holds 4 more chunks of G^T, X^T and packed X_c
     one = ws(16384, 0, 8 * gt_chunk)
-    assert 4 * gt_chunk - acc32 < one - base <= 4 * (gt_chunk + xt_chunk) - acc32 + 4096
-    # a budget of one chunk: 3 chunks less of G^T and X^T than the default
+    assert 4 * gt_chunk - acc32 < one - base <= 4 * (gt_chunk + 2 * xt_chunk) - acc32 + 4096
+    # a budget of one chunk: 3 chunks less of G^T, X^T and packed X_c than the default
     small = ws(16384, 0, gt_chunk)
-    assert 3 * gt_chunk <= base - small <= 3 * (gt_chunk + xt_chunk) + (64 << 20)
+    assert 3 * gt_chunk <= base - small <= 3 * (gt_chunk + 2 * xt_chunk) + (64 << 20)
     # weight-dtype mode keeps no fp32 accumulator
     assert ws(16384, 1, 0) <= base - acc32
 
