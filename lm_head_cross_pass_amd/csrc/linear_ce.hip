@@ -1057,7 +1057,8 @@ LinearCeWorkspace linear_ce_workspace_layout(int64_t BT, int64_t D, int64_t V, i
   w.z_off = take(generic ? 0 : static_cast<size_t>(C) * w.ldv * 2);
   w.gt_off = take(static_cast<size_t>(w.ldv) * w.ldk * 2);
   // packed copies (gemm.h) of the products' B operands: X^T [D, ldk], W^T
-  // [D, ldv] and, for the fused path's logits, the chunk's X_c [C, D]
+  // [D, ldv] and, for the fused path's logits, the X_c [C, D] of each chunk of a
+  // group (packed together at the group's first chunk)
   w.xt_off = take(packed_bytes(D, w.ldk));
   w.wt_off = take(packed_bytes(D, w.ldv));
   w.xp_off = take(generic ? 0 : w.dw_group * packed_bytes(C, D));
