@@ -6,6 +6,12 @@ Two calls in a row on one GPU, the second with fewer rows, so the second
 reads the scratch after the first has left its contents there; each result
 must equal the workspace entry point's bit for bit (the same kernels run on
 the same inputs), which is tighter than the tolerances against the oracle.
+
+Because the entry point allocates nothing, a caller can capture it in a HIP
+graph: captured once on static buffers, the graph is replayed on new logits
+and targets written into those buffers, with eager work and synchronizations
+between the replays, and every replay must equal ce_fwd_bwd on the same
+inputs bit for bit.
 """
 import pytest
 import torch
@@ -73,3 +79,57 @@ def test_noalloc_rejects_more_rows_than_its_scratch():
                                  o[2].data_ptr(), stream)
     torch.cuda.synchronize()
     assert st == _lib.LMX_OK and int(o[1]) == B
+
+
+@pytest.mark.parametrize("in_place", (False, True))
+def test_noalloc_replayed_from_a_graph(in_place):
+    B, V, code, red, z = 1000, 50257, _lib.LMX_BF16, _lib.LMX_MEAN, 1e-4
+    x = torch.empty((B, V), dtype=torch.bfloat16, device=DEV)
+    t = torch.empty(B, dtype=torch.int64, device=DEV)
+    g = x if in_place else torch.empty_like(x)
+    o = _outs()
+
+    def call(stream):
+        return _lib.ce_fwd_bwd_noalloc(x.data_ptr(), g.data_ptr(), t.data_ptr(), B, V, code, -100,
+                                       red, z, o[0].data_ptr(), o[1].data_ptr(),
+                                       o[2].data_ptr(), stream)
+
+    inputs = [workloads.small_ce(B, V, dtype=torch.bfloat16, sigma=3.0, n_ignored=40 + 10 * i,
+                                 seed=100 + i, boost=8.0) for i in range(3)]
+    # an eager call first: the library looks up its scratch array's address on
+    # the device's first call, outside the capture
+    x.copy_(inputs[0][0].to(DEV))
+    t.copy_(inputs[0][1].to(DEV))
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        _lib.check("ce_fwd_bwd_noalloc", call(side.cuda_stream))
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _lib.check("ce_fwd_bwd_noalloc", call(torch.cuda.current_stream(DEV).cuda_stream))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    for logits, target in inputs + inputs[:1]:
+        # eager work of the program between replays: new inputs into the
+        # captured buffers, the reference call on copies of them
+        x.copy_(logits.to(DEV))
+        t.copy_(target.to(DEV))
+        x_ref = x.clone()
+        g_ref = x_ref if in_place else torch.empty_like(x_ref)
+        o_ref = _outs()
+        ws = torch.empty(_lib.ce_workspace_bytes(B, V, code), dtype=torch.uint8, device=DEV)
+        _lib.check("ce_fwd_bwd", _lib.ce_fwd_bwd(
+            x_ref.data_ptr(), g_ref.data_ptr(), t.data_ptr(), B, V, code, -100, red, z,
+            o_ref[0].data_ptr(), o_ref[1].data_ptr(), o_ref[2].data_ptr(), ws.data_ptr(),
+            ws.numel(), stream))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g, g_ref)
+        assert torch.equal(o[0], o_ref[0])
+        assert int(o[1]) == int(o_ref[1]) == int((target != -100).sum())
+        assert int(o[2]) == int(o_ref[2]) == 0
