@@ -483,3 +483,65 @@ def test_grad_weight_short_k_small_tile_tail(accum):
     assert float(loss) == pytest.approx(ref["loss"], rel=2e-3)
     assert _rel(gx, ref["grad_inputs"]) <= 1e-2
     assert _rel(gw, ref["grad_weight"]) <= 1e-2
+
+
+@pytest.mark.parametrize("accum", (0, 1))
+def test_linear_ce_replayed_from_a_graph(accum):
+    """linear_ce with a caller workspace allocates and synchronizes nothing, so
+    a HIP graph can capture a whole call (every chunk's launches): captured once
+    on static buffers, replayed on new inputs, weight and targets written into
+    them, with eager work and synchronizations between the replays; each
+    replay equals an eager call on the same inputs bit for bit (both
+    accumulation modes, several grad_weight groups, a ragged last chunk)."""
+    from lm_head_cross_pass_amd import _lib
+    BT, D, V, C = 1000, 128, 3000, 96
+    group = 3 * (3072 * 128 * 2)   # G^T of three chunks (ldv 3072, ldc 128)
+    X = torch.empty((BT, D), dtype=torch.bfloat16, device=DEV)
+    W = torch.empty((V, D), dtype=torch.bfloat16, device=DEV)
+    t = torch.empty(BT, dtype=torch.int64, device=DEV)
+    code = _lib.LMX_BF16
+    wsb = _lib.linear_ce_workspace_bytes(BT, D, V, code, C, accum, group)
+
+    def call(stream, gx, gw, out, ws):
+        _lib.check("linear_ce", _lib.linear_ce(
+            X.data_ptr(), W.data_ptr(), t.data_ptr(), BT, D, V, code, -100, _lib.LMX_MEAN, 1e-4,
+            C, accum, group, out[0:1].data_ptr(), gx.data_ptr(), gw.data_ptr(),
+            out[1:2].data_ptr(), out[2:3].data_ptr(), ws.data_ptr(), wsb, stream))
+
+    def buffers():
+        # the loss (fp32) and the flag (int32) fill half of their int64 slots:
+        # zeroed, so that the slots compare whole
+        return (torch.empty_like(X), torch.empty_like(W),
+                torch.zeros(4, dtype=torch.int64, device=DEV),
+                torch.empty(wsb, dtype=torch.uint8, device=DEV))
+
+    inputs = [workloads.small_linear_ce(BT, D, V, n_ignored=30 + 7 * i, seed=300 + i)
+              for i in range(3)]
+    gx, gw, out, ws = buffers()
+    X.copy_(inputs[0][0].to(DEV))
+    W.copy_(inputs[0][1].to(DEV))
+    t.copy_(inputs[0][2].to(DEV))
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        call(side.cuda_stream, gx, gw, out, ws)
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream(DEV).cuda_stream, gx, gw, out, ws)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    for Xh, Wh, th in inputs + inputs[:1]:
+        X.copy_(Xh.to(DEV))
+        W.copy_(Wh.to(DEV))
+        t.copy_(th.to(DEV))
+        rgx, rgw, rout, rws = buffers()
+        call(stream, rgx, rgw, rout, rws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gx, rgx) and torch.equal(gw, rgw)
+        assert torch.equal(out[:3], rout[:3])
+        assert int(out[1]) == int((th != -100).sum())
