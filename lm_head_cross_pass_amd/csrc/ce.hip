@@ -761,9 +761,12 @@ struct RowKernel {
 // With few rows per CU each workgroup walks only one or two rows, so the
 // reads of a row are not overlapped with the stores of another within a
 // workgroup; three workgroups per CU instead of two put more rows in flight
-// at once. [1024, 50257] bf16 rows with their gradient (a chunk of the
-// 8192 x 768 x 50257 linear cross-entropy): 1.2% off the whole linear call;
-// [4096, 50257]: 2.5% slower than two per CU, so only up to 4 rows per CU.
+// at once. Taken only where the caller asks (CeParams::few_rows) and at most
+// 4 rows per CU: the 1024-row chunks of the 8192 x 768 x 50257 linear
+// cross-entropy, whose logits were just written, run 33 against 40 us; on
+// logits read from HBM it depends on the width (768 to 1024 rows of 50256 or
+// 50257: 1 to 6% slower; of 40001 to 45001: 7 to 10% faster; [4096, 50257]:
+// 2.5% slower), so ce_fwd_bwd keeps two per CU.
 constexpr int64_t kFewRowsPerCu = 4;
 
 template <typename T, bool G>
@@ -849,7 +852,7 @@ int ce_rows_enqueue(const CeParams& p, int dtype, hipStream_t stream) {
       if (ks[i].capacity == 0 || ks[i].capacity >= need) { pick = &ks[i]; break; }
     }
     const void* fn = pick->fn;
-    if (pick->few_rows_fn != nullptr) {
+    if (p.few_rows && pick->few_rows_fn != nullptr) {
       const int cus = device_cus();
       if (cus <= 0) return LMX_ERR_HIP;
       if (p.B <= kFewRowsPerCu * cus) fn = pick->few_rows_fn;

@@ -21,6 +21,8 @@ struct CeParams {
   int64_t* n_valid_user;    // optional output
   int32_t* bad_user;        // optional output
   int negate;               // row outputs x[t] - lse instead of lse - x[t] (z must be 0)
+  int few_rows;             // 1: with few rows per CU, the row kernel may take its instance
+                            // with more workgroups per CU (the linear-CE chunk rows)
 };
 
 // N and the out-of-range flag over `target` (one workgroup, no zeroed memory needed).

@@ -1162,6 +1162,7 @@ int linear_ce_run(const LinearCeParams& p, void* ws_base, hipStream_t stream) {
       cp.reduction = LMX_SUM;   // the mean's 1/N enters in steps 5 and 6
       cp.n_valid_ws = n_ws;
       cp.row_loss = row_loss + r0;
+      cp.few_rows = 1;
       st = ce_rows_enqueue(cp, p.dtype, stream);
       if (st != LMX_OK) return st;
     }

@@ -143,11 +143,12 @@ def test_shapes_against_oracle(B, V, dtype):
 @pytest.mark.parametrize("B,V,dtype", ((1000, 50257, torch.bfloat16),
                                         (1000, 50257, torch.float16),
                                         (1000, 20000, torch.float32)))
-def test_few_rows_per_cu_with_rows_walked_twice(B, V, dtype):
-    """1000 rows of up to 6656 16-byte chunks: at most 4 rows per CU, where the
-    row kernel of this width runs in fewer registers with more workgroups
-    resident per CU (768 on 256 CUs), so some workgroups walk a second row;
-    every row against the oracle, in place and out of place, both reductions."""
+def test_more_rows_than_resident_workgroups(B, V, dtype):
+    """1000 rows of up to 6656 16-byte chunks: the row kernel of this width
+    runs two 512-thread workgroups per CU (512 on 256 CUs), so some workgroups
+    walk a second row; every row against the oracle, in place and out of place,
+    both reductions. (The linear-CE chunk rows take its instance with three
+    workgroups per CU; the linear-CE tests at V = 50257 cover it.)"""
     logits, target = workloads.small_ce(B, V, dtype=dtype, sigma=3.0, n_ignored=50,
                                         seed=17, boost=8.0)
     for red, z in (("mean", 1e-4), ("sum", 0.0)):
